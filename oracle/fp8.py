@@ -1,0 +1,249 @@
+"""fp8 (E4M3) low-bit attention: format, pre-pass and quantisation model.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources on the pages
+--------------------
+* FP8 doubles tensor throughput [real-time video generation FLOPS article
+  (sudonull.com), "Optymalizacje", FP8 item].
+* Q/K smoothing before the low-bit QK^T (the SageAttention2 approach) and
+  the value term as the remaining error [VC-Attention article (aikraft.ru),
+  §01].
+* V-Smooth: subtract a mean, quantise only the residual per channel in
+  E4M3, add the mean back using the online-softmax row sum, no second pass
+  [VC-Attention article, §02, Demean and Restore].
+* The E4M3 byte read as an integer is close to 8*log2(v) + 56 [VC-Attention
+  article, §03].
+
+Readings taken where the pages are silent (each also listed in the design
+notes): Q and K use one scale per 64-token block; K is smoothed by the mean
+of each 64-token block (or one global mean per head), and the per-block mean
+is compensated exactly by adding q_hat . k_mean_b to the scores of block b;
+V is smoothed by one per-channel mean over the sequence with one per-channel
+scale; P is quantised as E4M3(448 * 2^(t - M)) where t is the log2-domain
+score and M the integer ceiling of the row maximum of t; the row sum uses
+the unquantised P.
+
+Precision of the integer-valued decisions (codes): the pre-pass takes them
+in the precision the kernel takes them in, so the codes can be compared bit
+for bit:  means are fp64 sums of the bf16 inputs (exact here) divided in
+fp64 and rounded once to fp32;  residual = fp32(x - mean);  amax = max|r|;
+scale = fp32(amax / 448) and inv = fp32(448 / amax) (both from fp64
+quotients), or 1 and 0 when amax = 0;  code = E4M3_RNE(clamp(fp32(r * inv),
+-448, 448)).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .attention import _as_f64
+
+__all__ = [
+    "E4M3_MAX",
+    "e4m3_encode",
+    "e4m3_decode",
+    "e4m3_table",
+    "quantize_head",
+    "quantize",
+    "attention_fp8_model_head",
+    "attention_fp8_model",
+    "cosine",
+    "max_abs",
+    "mean_rel_l1",
+]
+
+E4M3_MAX = 448.0
+_MIN_NORMAL = 2.0 ** -6
+
+
+def e4m3_table() -> np.ndarray:
+    """Value of each of the 256 E4M3 codes, from the format definition:
+    1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field
+    0 holds subnormals m * 2^-9; 0x7F / 0xFF are NaN; there is no infinity."""
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * m * 2.0 ** -9
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_TABLE = e4m3_table()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round to the nearest E4M3 value, ties to even mantissa, after clamping
+    to +-448 (saturation).  Input is any float array (taken exactly in fp64);
+    output uint8 codes.  Negative values that round to zero give 0x80."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < _MIN_NORMAL
+    # subnormal range: multiples of 2^-9 (a * 2^9 is exact, rint is RNE)
+    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)  # 8 -> 0x08, the least normal
+    nrm = ~sub
+    f, E = np.frexp(a[nrm])            # a = f * 2^E, f in [0.5, 1)
+    e = E.astype(np.int64) - 1         # a = s * 2^e, s in [1, 2)
+    s = f * 2.0                        # exact
+    mant = np.rint((s - 1.0) * 8.0).astype(np.int64)  # exact scaling, RNE
+    carry = mant == 8
+    e = e + carry
+    mant = np.where(carry, 0, mant)
+    code[nrm] = ((e + 7) << 3) | mant
+    code = np.where(np.isnan(x), 0x7F, code)
+    return (code | (neg.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _scales(amax: np.ndarray):
+    """scale = fp32(amax/448), inv = fp32(448/amax); (1, 0) where amax == 0."""
+    amax = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    zero = amax == 0.0
+    safe = np.where(zero, 1.0, amax)
+    scale = np.where(zero, 1.0, safe / E4M3_MAX).astype(np.float32)
+    inv = np.where(zero, 0.0, E4M3_MAX / safe).astype(np.float32)
+    return scale, inv
+
+
+def _codes(r32: np.ndarray, inv32) -> np.ndarray:
+    """E4M3 codes of fp32(r * inv) clamped to +-448 (fp32 product, RNE)."""
+    prod = (r32.astype(np.float32) * np.asarray(inv32, dtype=np.float32)).astype(np.float32)
+    return e4m3_encode(np.clip(prod, -E4M3_MAX, E4M3_MAX))
+
+
+def _mean32(x32: np.ndarray, axis: int) -> np.ndarray:
+    """fp32(fp64 sum / n): the sum of bf16 values is exact in fp64 here."""
+    n = x32.shape[axis]
+    s = x32.astype(np.float64).sum(axis=axis)
+    return (s / float(n)).astype(np.float32)
+
+
+def quantize_head(q, k, v, block: int = 64, k_mean: str = "block"):
+    """fp8 pre-pass for one (b, h).  q, k, v: bf16 bits or exact values [S, D].
+
+    Returns a dict with uint8 codes q8, k8, v8 [S, D]; q_scale, k_scale
+    [nb] (nb = ceil(S / block)); k_mean [nb or 1, D]; v_mean, v_scale [D]
+    (all float32).  ``k_mean`` is "block" (one mean per block of ``block``
+    tokens, statistics over the valid tokens only) or "global" (one mean
+    per channel over the whole sequence)."""
+    q32 = _as_f64(q).astype(np.float32)
+    k32 = _as_f64(k).astype(np.float32)
+    v32 = _as_f64(v).astype(np.float32)
+    S, D = q32.shape
+    nb = -(-S // block)
+    out = {
+        "q8": np.empty((S, D), np.uint8), "k8": np.empty((S, D), np.uint8),
+        "q_scale": np.empty(nb, np.float32), "k_scale": np.empty(nb, np.float32),
+    }
+    if k_mean == "block":
+        kmean = np.empty((nb, D), np.float32)
+        for b in range(nb):
+            kmean[b] = _mean32(k32[b * block:(b + 1) * block], axis=0)
+        kmean_tok = np.repeat(kmean, block, axis=0)[:S]
+    elif k_mean == "global":
+        kmean = _mean32(k32, axis=0)[None, :]
+        kmean_tok = np.broadcast_to(kmean, (S, D))
+    else:
+        raise ValueError(k_mean)
+    kres = (k32 - kmean_tok).astype(np.float32)
+    for b in range(nb):
+        sl = slice(b * block, min(S, (b + 1) * block))
+        for name, src, dst in (("q", q32, "q8"), ("k", kres, "k8")):
+            amax = np.max(np.abs(src[sl]))
+            sc, inv = _scales(amax)
+            out[name + "_scale"][b] = sc
+            out[dst][sl] = _codes(src[sl], inv)
+    out["k_mean"] = kmean
+    vmean = _mean32(v32, axis=0)
+    vres = (v32 - vmean[None, :]).astype(np.float32)
+    vsc, vinv = _scales(np.max(np.abs(vres), axis=0))
+    out["v_mean"], out["v_scale"] = vmean, vsc
+    out["v8"] = _codes(vres, vinv[None, :])
+    return out
+
+
+def quantize(q, k, v, block: int = 64, k_mean: str = "block"):
+    """quantize_head over [B, H, S, D]; arrays gain leading [B, H] axes."""
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    B, H = q.shape[:2]
+    parts = [[quantize_head(q[b, h], k[b, h], v[b, h], block, k_mean) for h in range(H)]
+             for b in range(B)]
+    return {key: np.stack([np.stack([parts[b][h][key] for h in range(H)]) for b in range(B)])
+            for key in parts[0][0]}
+
+
+def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
+                             p_quant: bool = True, p_scale: float = E4M3_MAX,
+                             chunk: int = 256) -> np.ndarray:
+    """Quantisation model of the fp8 attention for one head, in fp64.
+
+    Steps: dequantise Q_hat = dec(q8) q_scale, K_hat = dec(k8) k_scale,
+    V_hat = dec(v8) v_scale;  s_ij = scale (Q_hat_i . K_hat_j + Q_hat_i .
+    k_mean_b(j));  t = log2(e) s;  M_i = ceil(max_j t_ij);  p = 2^(t - M);
+    l_i = sum_j p_ij;  w = dec(E4M3(p_scale p)) / p_scale (or w = p without
+    P quantisation);  O_i = (sum_j w_ij V_hat_j) / l_i + v_mean.
+    """
+    S, D = qz["q8"].shape
+    nb = qz["q_scale"].shape[0]
+    tok_blk = np.arange(S) // block
+    qh = e4m3_decode(qz["q8"]) * qz["q_scale"].astype(np.float64)[tok_blk][:, None]
+    kh = e4m3_decode(qz["k8"]) * qz["k_scale"].astype(np.float64)[tok_blk][:, None]
+    vh = e4m3_decode(qz["v8"]) * qz["v_scale"].astype(np.float64)[None, :]
+    km = qz["k_mean"].astype(np.float64)
+    kmean_tok = km[tok_blk] if km.shape[0] == nb and nb > 1 else np.broadcast_to(km[0], (S, D))
+    keff = kh + kmean_tok          # q.(k_res + k_mean) = q.k_res + q.k_mean
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, D), np.float64)
+    log2e = 1.0 / math.log(2.0)
+    for r0 in range(0, rows.size, chunk):
+        rr = rows[r0:r0 + chunk]
+        t = (qh[rr] @ keff.T) * (float(np.float64(scale)) * log2e)
+        M = np.ceil(t.max(axis=1, keepdims=True))
+        p = np.exp2(t - M)
+        l = p.sum(axis=1, keepdims=True)
+        w = e4m3_decode(e4m3_encode(p * p_scale)) / p_scale if p_quant else p
+        out[r0:r0 + chunk] = (w @ vh) / l + qz["v_mean"].astype(np.float64)[None, :]
+    return out
+
+
+def attention_fp8_model(qz: dict, scale: float, rows=None, **kw) -> np.ndarray:
+    """attention_fp8_model_head over the [B, H] axes of ``quantize`` output."""
+    B, H = qz["q8"].shape[:2]
+    n = qz["q8"].shape[2] if rows is None else len(rows)
+    out = np.empty((B, H, n, qz["q8"].shape[3]), np.float64)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = attention_fp8_model_head({key: val[b, h] for key, val in qz.items()},
+                                                 scale, rows, **kw)
+    return out
+
+
+# Error measures used by the tolerance checks (fp64 sums).
+def cosine(a, b) -> float:
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / math.sqrt(float(a @ a) * float(b @ b)))
+
+
+def max_abs(a, b) -> float:
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def mean_rel_l1(a, ref) -> float:
+    """sum |a - ref| / sum |ref| (robust near zero)."""
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(a - ref).sum() / np.abs(ref).sum())
