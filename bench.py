@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Benchmark of the spatiotemporal self-attention forward on one MI355X.
+
+Default: the 720p Wan2.1-14B-shaped self-attention (B=1, H=40, S=75,600,
+D=128, bf16, 4 outlier channels per head in K and V) through the C ABI
+(vdit_attn_fwd), W warm-up launches then K timed launches bracketed by HIP
+events on the launch stream.  Prints ONE JSON line with the throughput in
+TFLOP/s (4 B H S^2 D per launch), the roofline of the attention kernel
+against the dense bf16 MFMA peak, the fp8 path (pre-pass + fp8 attention on
+the same tensors) timed the same way, and the fp64 CPU oracle timed on a
+bounded row sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-fp8]
+                  [--no-cpu-baseline] [--cpu-seconds T]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from video_diffusion_transformer_vdit_amd import binding, inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "wan2.1-14b-720p"
+METRIC = "attention TFLOP/s & % of bf16 MFMA peak at S=75,600 H=40 D=128"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_launches(fn, steps, warmup):
+    """Average ms per launch over `steps` launches after `warmup` ones, with
+    HIP events recorded on torch's current stream (the launch stream)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, q, k, v, scale, seconds):
+    """fp64 oracle (as it stands) on head 0, 256-row chunks until `seconds`
+    have elapsed; rate scaled to TFLOP/s of the same attention arithmetic."""
+    from oracle import attention as oa
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rows_done = 0
+    t0 = time.perf_counter()
+    chunk = 256
+    start = 0
+    while True:
+        rows = np.arange(start, min(w.S, start + chunk))
+        oa.attention_head(q[0, 0], k[0, 0], v[0, 0], scale, rows=rows)
+        rows_done += rows.size
+        start = (start + chunk) % w.S
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    flop = rows_done * 4.0 * w.S * w.D
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{rows_done} query rows of head 0 of {w.name} (S={w.S}), fp64 numpy, "
+                   f"{dt:.1f} s; full call extrapolates to {w.flop / (flop / dt):.0f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange inside attention).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+
+    w = inputs.get_workload(args.workload)
+    scale = float(np.float32(1.0 / math.sqrt(w.D)))
+    log(f"[bench] generating {w.name} {w.shape}")
+    qb, kb, vb = inputs.make_inputs(w)
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    o = torch.empty_like(q)
+    log("[bench] bf16 attention")
+    ms = time_launches(lambda: binding.vdit_attn_fwd(q, k, v, o=o, scale=scale), args.steps, args.warmup)
+    tflops = w.flop / (ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian Q/K/V with the workload's structure; no model weights)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "structure": w.structure, "causal": False, "scale": scale},
+        "peak_fraction": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16_kernel",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flop_per_launch": w.flop,
+            "algorithmic_bytes_per_launch": 4 * w.B * w.H * w.S * w.D * 2,
+        },
+    }
+
+    if not args.no_fp8:
+        log("[bench] fp8 pre-pass + attention")
+        z = binding.vdit_attn_quant_fp8(q, k, v)
+        o8 = torch.empty_like(q)
+        ms_q = time_launches(lambda: binding.vdit_attn_quant_fp8(q, k, v, out=z), args.steps, args.warmup)
+        ms_a = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o8), args.steps, args.warmup)
+        prepass_bytes = w.B * w.H * w.S * w.D * (2 * 3 + 2 + 1 + 2 + 1)  # reads Q,K,V,V(again); writes 3 codes
+        result["fp8"] = {
+            "attention_ms": round(ms_a, 4),
+            "attention_tflops": round(w.flop / (ms_a * 1e-3) / 1e12, 2),
+            "attention_peak_fraction": round(w.flop / (ms_a * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "prepass_ms": round(ms_q, 4),
+            "prepass_gbs": round(prepass_bytes / (ms_q * 1e-3) / 1e9, 1),
+            "combined_tflops": round(w.flop / ((ms_a + ms_q) * 1e-3) / 1e12, 2),
+        }
+        del z, o8
+    del o
+    torch.cuda.synchronize()
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, scale, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

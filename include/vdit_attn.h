@@ -1,0 +1,131 @@
+/*
+ * vdit_attn.h - C ABI of the MI355X (gfx950) spatiotemporal self-attention
+ * forward library (libvdit_attn.so).
+ *
+ * The operation.  A video DiT flattens a clip into one sequence of S
+ * spatiotemporal tokens and runs full, non-causal self-attention over all of
+ * them in every layer (VC-Attention article (aikraft.ru), section 01); the
+ * score matrix is quadratic in S and, with its projections, about 82% of a
+ * Wan2.1-14B layer's FLOPs at S = 75,600 (real-time video generation FLOPS
+ * article (sudonull.com), FLOP list).  For every batch b, head h and query i:
+ *
+ *     O[b,h,i,:] = sum_j softmax_j(scale * <Q[b,h,i,:], K[b,h,j,:]>) V[b,h,j,:]
+ *
+ * computed flash-style (the S x S matrix is never stored; same article,
+ * "Optymalizacje", FlashAttention item).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are caller-owned DEVICE memory, layout [B, H, S, D], contiguous,
+ *    D fastest.  D must be 128.  Pointers must be 16-byte aligned.
+ *  - The library never allocates, frees or synchronises; work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and runs
+ *    asynchronously.  Buffers must stay valid until the stream reaches it.
+ *  - Arguments are validated before any HIP call.  Errors are returned, never
+ *    thrown.  On VDIT_ERR_HIP the launch failed; vdit_last_error() gives the
+ *    HIP error text of the calling thread's last failure.
+ *  - Results are deterministic: no atomics, fixed reduction order.
+ */
+#ifndef VDIT_ATTN_H
+#define VDIT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VDIT_ABI_VERSION 1
+#define VDIT_HEAD_DIM 128
+#define VDIT_FP8_BLOCK 64 /* tokens per Q/K fp8 scale block and K mean block */
+
+typedef enum vdit_status {
+  VDIT_OK = 0,
+  VDIT_ERR_INVALID_ARG = 1, /* null/misaligned pointer, B/H/S < 1, bad scale */
+  VDIT_ERR_UNSUPPORTED = 2, /* D != 128, unknown dtype, too large, bad mode */
+  VDIT_ERR_HIP = 3          /* a HIP launch or runtime call failed */
+} vdit_status;
+
+typedef enum vdit_dtype {
+  VDIT_DTYPE_BF16 = 0 /* q, k, v, o are bfloat16 */
+} vdit_dtype;
+
+/* Version of this ABI (VDIT_ABI_VERSION the library was built with). */
+int vdit_abi_version(void);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* vdit_status_str(int status);
+
+/* Text of the calling thread's last error ("" if none). */
+const char* vdit_last_error(void);
+
+/*
+ * bf16 attention forward.
+ *   q, k, v : [B,H,S,D] bf16 inputs.   o : [B,H,S,D] bf16 output.
+ *   scale   : softmax scale (usually 1/sqrt(D)); finite and > 0.
+ *   dtype   : VDIT_DTYPE_BF16.
+ * Softmax and accumulation are fp32; P is rounded to bf16 before the P.V
+ * product; O is rounded to bf16 (nearest even).  o may not alias q, k or v.
+ */
+vdit_status vdit_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                          int B, int H, int S, int D, float scale, int dtype,
+                          void* stream);
+
+/*
+ * fp8 pre-pass: quantise and smooth bf16 Q, K, V to E4M3 (OCP E4M3FN, max 448)
+ * for vdit_attn_fwd_fp8.  Follows V-Smooth (VC-Attention article, section 02:
+ * subtract a mean, quantise only the residual per channel in E4M3) and the
+ * Q/K smoothing of section 01.  With nb = ceil(S / 64):
+ *   q8, k8, v8  : [B,H,S,D] uint8 E4M3 codes (out).
+ *   q_scale     : [B,H,nb] float, amax/448 of each 64-token Q block (out).
+ *   k_mean      : [B,H,k_mean_blocks,D] float (out); k_mean_blocks = nb gives
+ *                 one mean per 64-token block (valid tokens only), = 1 one
+ *                 mean per channel over the whole sequence.
+ *   k_scale     : [B,H,nb] float, amax/448 of each block of K - k_mean (out).
+ *   v_mean      : [B,H,D] float, per-channel mean of V over the sequence (out).
+ *   v_scale     : [B,H,D] float, per-channel amax/448 of V - v_mean (out).
+ *   workspace   : caller-owned device scratch of at least
+ *                 vdit_attn_quant_fp8_workspace_size(B,H,S,D,k_mean_blocks)
+ *                 bytes, 16-byte aligned; holds the per-block V (and global
+ *                 K) partial statistics between the three launches.  Its
+ *                 contents on entry do not matter; calls that share one
+ *                 workspace must be ordered on one stream.
+ * Means are fp64 sums divided in fp64 and rounded once to fp32; residuals
+ * are fp32; codes are E4M3 round-to-nearest-even of clamp(r * fp32(448/amax),
+ * +-448); a block or channel with amax = 0 gets scale 1 and zero codes.
+ * Float arrays must be 16-byte aligned.
+ */
+vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v,
+                                void* q8, void* k8, void* v8,
+                                float* q_scale, float* k_scale,
+                                float* k_mean, int k_mean_blocks,
+                                float* v_mean, float* v_scale,
+                                void* workspace, size_t workspace_bytes,
+                                int B, int H, int S, int D, void* stream);
+
+/* Bytes of workspace vdit_attn_quant_fp8 needs (0 for invalid shapes). */
+size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean_blocks);
+
+/*
+ * fp8 attention forward on the pre-pass outputs (same shapes as above).
+ * Scores: s_ij = q_scale_b(i) k_scale_b(j) (q8_i . k8_j) + q_hat_i . k_mean_b(j)
+ * (the second term restores a per-block K mean exactly; with k_mean_blocks = 1
+ * it is a per-row constant and is dropped).  Softmax in the log2 domain with
+ * an integer running reference; P is quantised as E4M3(448 * p) for the fp8
+ * P.V product while the row sum uses the fp32 p; the epilogue adds v_mean
+ * back (VC-Attention article, section 02, Restore):
+ *   o = v_scale * (sum_j P8_ij v8_j) / (448 l_i) + v_mean, bf16 out.
+ * Float arrays must be 16-byte aligned.
+ */
+vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                              const float* q_scale, const float* k_scale,
+                              const float* k_mean, int k_mean_blocks,
+                              const float* v_mean, const float* v_scale,
+                              void* o, int B, int H, int S, int D, float scale,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDIT_ATTN_H */

@@ -1,0 +1,61 @@
+"""Helpers for the GPU parity tests: host<->device transfer of bf16 bit
+patterns, oracle rounding to bf16 and the tolerance bars."""
+
+import os
+import sys
+
+import numpy as np
+
+from video_diffusion_transformer_vdit_amd import inputs
+
+# bf16 bars (against the oracle rounded to bf16, the closest an output in
+# bf16 can get): max-abs <= 1e-2, L1 mean-rel <= 2e-3.
+BF16_MAX_ABS = 1e-2
+BF16_MEAN_REL = 2e-3
+# fp8 bars: cosine >= 0.999, max-abs <= 5e-2 (used against the fp64
+# quantisation model, see test_parity_fp8.py), plus an L1 mean-rel bar.
+FP8_COS = 0.999
+FP8_MAX_ABS = 5e-2
+FP8_MODEL_MEAN_REL = 1e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def to_dev_any(arr):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def bits_of(t):
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32_of(t):
+    return inputs.bf16_bits_to_f32(bits_of(t)).astype(np.float64)
+
+
+def round_bf16(x):
+    return inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(np.asarray(x, np.float32))).astype(np.float64)
+
+
+def sample_rows(S, n_random=96, tile=128, seed=0):
+    """First and last rows, every row of the ragged last query tile, and a
+    seeded random sample."""
+    g = np.random.default_rng(seed)
+    last_tile = np.arange((S - 1) // tile * tile, S)
+    rows = np.concatenate([[0, 1, S // 2], last_tile, g.choice(S, size=min(n_random, S), replace=False)])
+    return np.unique(rows)
+
+
+def workload_heads(H):
+    return sorted({0, H // 2, H - 1})

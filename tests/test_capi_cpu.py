@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every symbol the header declares, and
+rejects bad arguments before any HIP call (so this runs without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_diffusion_transformer_vdit_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vdit_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="library not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vdit_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["vdit_attn_fwd", "vdit_attn_quant_fp8", "vdit_attn_fwd_fp8", "vdit_status_str",
+              "vdit_last_error", "vdit_abi_version", "vdit_attn_quant_fp8_workspace_size"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) <= set(binding.SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    lib = binding.load()
+    assert lib.vdit_abi_version() == 1
+    assert lib.vdit_status_str(0) == b"ok"
+    assert lib.vdit_status_str(1) == b"invalid argument"
+    assert lib.vdit_status_str(2) == b"unsupported argument"
+    assert lib.vdit_status_str(3) == b"HIP runtime error"
+    assert lib.vdit_status_str(99) == b"unknown status"
+
+
+A = 0x10000  # fake, 16-byte aligned addresses: validation never dereferences
+
+
+def fwd(q=A, k=A * 2, v=A * 3, o=A * 4, B=1, H=1, S=16, D=128, scale=0.1, dtype=0):
+    lib = binding.load()
+    st = lib.vdit_attn_fwd(q, k, v, o, B, H, S, D, scale, dtype, None)
+    return st, lib.vdit_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), 1, "null pointer: q"),
+    (dict(o=None), 1, "null pointer: o"),
+    (dict(k=A + 8), 1, "not 16-byte aligned: k"),
+    (dict(B=0), 1, "B, H and S"),
+    (dict(H=-1), 1, "B, H and S"),
+    (dict(S=0), 1, "B, H and S"),
+    (dict(D=64), 2, "D = 128"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(scale=float("inf")), 1, "scale"),
+    (dict(scale=-1.0), 1, "scale"),
+    (dict(dtype=1), 2, "dtype"),
+    (dict(o=A, q=A), 1, "overlaps"),
+    (dict(B=1 << 16, H=1 << 16, S=1 << 10), 2, "too large"),
+])
+def test_fwd_validation(kw, status, msg):
+    st, err = fwd(**kw)
+    assert st == status and msg in err, (st, err)
+
+
+def test_fp8_validation():
+    lib = binding.load()
+    S = 200
+    nb = 4
+    ws = lib.vdit_attn_quant_fp8_workspace_size(1, 2, S, 128, nb)
+    assert ws > 0
+    assert lib.vdit_attn_quant_fp8_workspace_size(1, 2, S, 128, 3) == 0
+    assert lib.vdit_attn_quant_fp8_workspace_size(1, 2, S, 64, nb) == 0
+    args = [A] * 9
+    st = lib.vdit_attn_quant_fp8(*args[:9], nb, A, A, A, ws - 1, 1, 2, S, 128, None)
+    assert st == 1 and b"workspace too small" in lib.vdit_last_error()
+    st = lib.vdit_attn_quant_fp8(*args[:9], 2, A, A, A, ws, 1, 2, S, 128, None)
+    assert st == 2 and b"k_mean_blocks" in lib.vdit_last_error()
+    st = lib.vdit_attn_quant_fp8(*args[:9], nb, A, A, None, ws, 1, 2, S, 128, None)
+    assert st == 1 and b"workspace" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8(A, A, A, A, A, A, nb, A, A, A, 1, 2, S, 128, 0.0, None)
+    assert st == 1 and b"scale" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8(A, A, A, A, A, A, 5, A, A, A, 1, 2, S, 128, 0.1, None)
+    assert st == 2 and b"k_mean_blocks" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8(A, A, A, A + 4, A, A, nb, A, A, A, 1, 2, S, 128, 0.1, None)
+    assert st == 1 and b"q_scale" in lib.vdit_last_error()
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.vdit_attn_fwd(x, x, x, o=x.clone())
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _load_fresh(str(tmp_path / "nope.so"))
+
+
+def _load_fresh(path):
+    saved = binding._lib
+    binding._lib = None
+    try:
+        return binding.load(path)
+    finally:
+        binding._lib = saved

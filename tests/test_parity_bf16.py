@@ -1,0 +1,140 @@
+"""GPU parity of the bf16 attention (through the C ABI) against the fp64
+oracle, on the seeded workloads, a shape sweep with ragged tails, and the
+definition's invariants.  Bars (against the oracle rounded to bf16):
+max-abs <= 1e-2 and L1 mean-rel <= 2e-3."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as oa
+from oracle import fp8 as ofp8
+from video_diffusion_transformer_vdit_amd import binding, inputs
+
+from gpu_util import (BF16_MAX_ABS, BF16_MEAN_REL, bits_of, f32_of, log, round_bf16,
+                      sample_rows, to_dev, workload_heads)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = float(np.float32(1.0 / math.sqrt(128)))
+
+
+def run(q_bits, k_bits, v_bits, scale=SCALE):
+    import torch
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    o = binding.vdit_attn_fwd(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def check_close(got, ref, what):
+    ref_b = round_bf16(ref)
+    ma = ofp8.max_abs(got, ref_b)
+    mr = ofp8.mean_rel_l1(got, ref_b)
+    mr_raw = ofp8.mean_rel_l1(got, ref)
+    log(f"{what}: max_abs={ma:.3e} mean_rel(bf16 oracle)={mr:.3e} mean_rel(raw)={mr_raw:.3e}")
+    assert ma <= BF16_MAX_ABS, (what, ma)
+    assert mr <= BF16_MEAN_REL, (what, mr)
+
+
+def test_tiny_workload_full():
+    w = inputs.get_workload("tiny-3x16x16")
+    q, k, v = inputs.make_inputs(w)
+    log(f"tiny: {w.shape}")
+    got = f32_of(run(q, k, v))
+    ref = oa.attention(q, k, v, SCALE)
+    check_close(got, ref, "tiny")
+
+
+@pytest.mark.parametrize("S", [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 127, 128, 129, 200, 1000])
+@pytest.mark.parametrize("B,H", [(1, 1), (2, 3)])
+def test_shape_sweep(S, B, H):
+    g = np.random.default_rng(S * 7 + B * 3 + H)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((B, H, S, 128)).astype(np.float32)) for _ in range(3)]
+    log(f"sweep B={B} H={H} S={S}")
+    got = f32_of(run(*x))
+    ref = oa.attention(*x, SCALE)
+    check_close(got, ref, f"sweep B={B} H={H} S={S}")
+
+
+def test_scales():
+    g = np.random.default_rng(5)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((1, 2, 300, 128)).astype(np.float32)) for _ in range(3)]
+    for scale in (1e-4, 0.02, 0.3):
+        got = f32_of(run(*x, scale=scale))
+        check_close(got, oa.attention(*x, scale), f"scale={scale}")
+
+
+def test_single_key_returns_value_exactly():
+    g = np.random.default_rng(1)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((1, 3, 1, 128)).astype(np.float32)) for _ in range(3)]
+    got = bits_of(run(*x))
+    assert np.array_equal(got, x[2])
+
+
+def test_constant_v_returns_constant():
+    g = np.random.default_rng(2)
+    B, H, S = 1, 2, 777
+    q = inputs.f32_to_bf16_bits(g.standard_normal((B, H, S, 128)).astype(np.float32) * 3)
+    k = inputs.f32_to_bf16_bits(g.standard_normal((B, H, S, 128)).astype(np.float32) * 3)
+    row = inputs.f32_to_bf16_bits(g.standard_normal(128).astype(np.float32))
+    v = np.broadcast_to(row, (B, H, S, 128)).copy()
+    got = f32_of(run(q, k, v))
+    want = np.broadcast_to(inputs.bf16_bits_to_f32(row).astype(np.float64), got.shape)
+    # P is rounded to bf16 but the normaliser is the fp32 sum: relative 2^-8 at most
+    assert np.max(np.abs(got - want) / (np.abs(want) + 1e-30)) <= 2 ** -7
+
+
+def test_deterministic_and_tail_guard():
+    """Two launches give identical bits, and the ragged tail writes nothing
+    outside O (guard regions around the output keep their sentinel)."""
+    import torch
+    g = np.random.default_rng(3)
+    B, H, S = 2, 3, 129
+    x = [to_dev(inputs.f32_to_bf16_bits(g.standard_normal((B, H, S, 128)).astype(np.float32)))
+         for _ in range(3)]
+    n = B * H * S * 128
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), -7.0, dtype=torch.bfloat16, device="cuda")
+    o = buf[guard:guard + n].view(B, H, S, 128)
+    binding.vdit_attn_fwd(*x, o=o, scale=SCALE)
+    o2 = binding.vdit_attn_fwd(*x, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert bool((buf[:guard] == -7.0).all()) and bool((buf[guard + n:] == -7.0).all())
+
+
+def test_k_offset_is_output_neutral():
+    """A per-channel K offset shifts each row of scores by a constant."""
+    g = np.random.default_rng(4)
+    B, H, S = 1, 2, 500
+    q, k, v = (g.standard_normal((B, H, S, 128)).astype(np.float32) for _ in range(3))
+    off = g.normal(0, 0.5, 128).astype(np.float32)
+    qb, kb, vb = (inputs.f32_to_bf16_bits(t) for t in (q, k, v))
+    kb2 = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(kb) + off)
+    a, b = f32_of(run(qb, kb, vb)), f32_of(run(qb, kb2, vb))
+    ref2 = oa.attention(qb, kb2, vb, SCALE)
+    check_close(b, ref2, "k+offset")
+    assert ofp8.max_abs(a, b) <= 2 * BF16_MAX_ABS
+
+
+@pytest.mark.parametrize("name", ["wan2.1-1.3b-480p", "wan2.2-720p-16x", "wan2.1-14b-720p"])
+def test_full_size_workload_sampled(name):
+    """Full-size launch (the configuration the benchmark times); oracle rows
+    sampled on three heads, including every row of the ragged last tile."""
+    import torch
+    w = inputs.get_workload(name)
+    log(f"{name}: generating {w.shape}")
+    q, k, v = inputs.make_inputs(w)
+    log(f"{name}: launching")
+    o = run(q, k, v)
+    rows = sample_rows(w.S)
+    heads = workload_heads(w.H)
+    got_all = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+    del o
+    torch.cuda.empty_cache()
+    for i, h in enumerate(heads):
+        log(f"{name}: oracle head {h} ({rows.size} rows)")
+        ref = oa.attention_head(q[0, h], k[0, h], v[0, h], SCALE, rows=rows)
+        check_close(got_all[i], ref, f"{name} head {h}")

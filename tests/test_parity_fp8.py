@@ -1,0 +1,177 @@
+"""GPU parity of the fp8 path (through the C ABI).
+
+* The pre-pass is integer work decided in a stated precision: codes, scales
+  and means must equal the oracle's bit for bit.
+* The fp8 attention kernel, fed the oracle's quantised tensors, is compared
+  with the fp64 quantisation model: cosine >= 0.999, max-abs <= 5e-2 and L1
+  mean-rel <= 1e-2 against the model rounded to bf16.
+* End to end (GPU pre-pass + GPU attention) against the unquantised truth the
+  error must stay within the floor that ideal quantisation itself reaches
+  (the model's own error against the truth on the same rows), plus a margin.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as oa
+from oracle import fp8 as ofp8
+from video_diffusion_transformer_vdit_amd import binding, inputs
+
+from gpu_util import (FP8_COS, FP8_MAX_ABS, FP8_MODEL_MEAN_REL, f32_of, log, round_bf16,
+                      sample_rows, to_dev, to_dev_any, workload_heads)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = float(np.float32(1.0 / math.sqrt(128)))
+KEYS = ["q8", "k8", "v8", "q_scale", "k_scale", "k_mean", "v_mean", "v_scale"]
+
+
+def gpu_quant(q, k, v, k_mean_blocks=None):
+    import torch
+    z = binding.vdit_attn_quant_fp8(to_dev(q), to_dev(k), to_dev(v), k_mean_blocks=k_mean_blocks)
+    torch.cuda.synchronize()
+    return z
+
+
+def compare_quant(zg, zo, heads=None, what=""):
+    for key in KEYS:
+        g = zg[key].cpu().numpy()
+        o = zo[key]
+        if heads is not None:
+            g = g[:, heads]
+        if not np.array_equal(g, o):
+            bad = np.argwhere(g != o)
+            raise AssertionError(f"{what} {key}: {len(bad)} mismatches, first at {bad[:3].tolist()}: "
+                                 f"gpu={g[tuple(bad[0])]} oracle={o[tuple(bad[0])]}")
+
+
+def rand_bits(shape, seed, scale=1.0, offset=0.0):
+    g = np.random.default_rng(seed)
+    return inputs.f32_to_bf16_bits((g.standard_normal(shape) * scale + offset).astype(np.float32))
+
+
+@pytest.mark.parametrize("S", [1, 17, 64, 65, 129, 1000])
+@pytest.mark.parametrize("mode", ["block", "global"])
+def test_prepass_bit_exact_sweep(S, mode):
+    B, H = 2, 2
+    q, k, v = rand_bits((B, H, S, 128), 1), rand_bits((B, H, S, 128), 2, 2.0, 0.3), \
+        rand_bits((B, H, S, 128), 3, 1.5, -4.0)
+    nb = -(-S // 64)
+    log(f"prepass sweep S={S} mode={mode}")
+    zg = gpu_quant(q, k, v, nb if mode == "block" else 1)
+    zo = ofp8.quantize(q, k, v, k_mean=mode)
+    compare_quant(zg, zo, what=f"S={S} {mode}")
+
+
+def test_prepass_constant_inputs():
+    B, H, S = 1, 1, 130
+    q = np.full((B, H, S, 128), inputs.f32_to_bf16_bits(np.array([0.5], np.float32))[0], np.uint16)
+    k = np.full_like(q, inputs.f32_to_bf16_bits(np.array([-3.0], np.float32))[0])
+    v = np.full_like(q, inputs.f32_to_bf16_bits(np.array([2.0], np.float32))[0])
+    zg = gpu_quant(q, k, v)
+    zo = ofp8.quantize(q, k, v)
+    compare_quant(zg, zo, what="constant")
+    assert np.all(zg["v8"].cpu().numpy() == 0) and np.all(zg["v_scale"].cpu().numpy() == 1.0)
+
+
+@pytest.mark.parametrize("name", ["tiny-3x16x16", "wan2.1-14b-720p-fp8"])
+def test_prepass_bit_exact_workload(name):
+    import torch
+    w = inputs.get_workload(name)
+    log(f"{name}: generating")
+    q, k, v = inputs.make_inputs(w)
+    heads = workload_heads(w.H)
+    log(f"{name}: GPU pre-pass")
+    zg = gpu_quant(q, k, v)
+    log(f"{name}: oracle pre-pass on heads {heads}")
+    zo = ofp8.quantize(q[:, heads], k[:, heads], v[:, heads])
+    compare_quant(zg, zo, heads, name)
+    del zg
+    torch.cuda.empty_cache()
+
+
+def check_model(got, ref, what):
+    ref_b = round_bf16(ref)
+    cos = ofp8.cosine(got, ref_b)
+    ma = ofp8.max_abs(got, ref_b)
+    mr = ofp8.mean_rel_l1(got, ref_b)
+    log(f"{what} vs quant model: cos={cos:.7f} max_abs={ma:.3e} mean_rel={mr:.3e}")
+    assert cos >= FP8_COS and ma <= FP8_MAX_ABS and mr <= FP8_MODEL_MEAN_REL, what
+
+
+def quantize_threaded(q, k, v, threads=8):
+    """ofp8.quantize_head over every (b, h), heads in parallel threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    B, H = q.shape[:2]
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda bh: ofp8.quantize_head(q[bh], k[bh], v[bh]), jobs))
+    return {key: np.stack([p[key] for p in parts]).reshape((B, H) + parts[0][key].shape)
+            for key in parts[0]}
+
+
+def zdev(zo):
+    return {key: to_dev_any(zo[key]) for key in KEYS}
+
+
+@pytest.mark.parametrize("mode", ["block", "global"])
+@pytest.mark.parametrize("S,seed", [(1, 1), (63, 2), (64, 3), (200, 4), (1000, 5)])
+def test_attention_vs_quant_model_sweep(S, seed, mode):
+    import torch
+    B, H = 1, 2
+    q, k, v = rand_bits((B, H, S, 128), seed), rand_bits((B, H, S, 128), seed + 10, 1.0, 0.5), \
+        rand_bits((B, H, S, 128), seed + 20, 1.0, 1.0)
+    zo = ofp8.quantize(q, k, v, k_mean=mode)
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE)
+    torch.cuda.synchronize()
+    got = f32_of(o)
+    ref = ofp8.attention_fp8_model(zo, SCALE)
+    check_model(got, ref, f"S={S} {mode}")
+
+
+@pytest.mark.parametrize("name", ["tiny-3x16x16", "wan2.1-14b-720p-fp8"])
+def test_attention_vs_quant_model_workload(name):
+    """Full-size launch on the oracle's quantised tensors; model rows sampled."""
+    import torch
+    w = inputs.get_workload(name)
+    q, k, v = inputs.make_inputs(w)
+    log(f"{name}: oracle pre-pass (all heads)")
+    zo = quantize_threaded(q, k, v)
+    del q, k, v
+    log(f"{name}: GPU fp8 attention")
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE)
+    torch.cuda.synchronize()
+    rows = np.arange(w.S) if w.S <= 1024 else sample_rows(w.S, n_random=64)
+    heads = workload_heads(w.H)
+    got = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+    del o
+    for i, h in enumerate(heads):
+        zh = {key: val[0, h] for key, val in zo.items()}
+        ref = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows)
+        check_model(got[i], ref, f"{name} head {h}")
+
+
+@pytest.mark.parametrize("name", ["tiny-3x16x16", "wan2.1-14b-720p-fp8"])
+def test_end_to_end_within_quantisation_floor(name):
+    import torch
+    w = inputs.get_workload(name)
+    q, k, v = inputs.make_inputs(w)
+    z = gpu_quant(q, k, v)
+    o = binding.vdit_attn_fwd_fp8(z, scale=SCALE)
+    torch.cuda.synchronize()
+    rows = np.arange(w.S) if w.S <= 1024 else sample_rows(w.S, n_random=32)
+    heads = workload_heads(w.H)[:2]
+    got = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+    del o, z
+    for i, h in enumerate(heads):
+        truth = oa.attention_head(q[0, h], k[0, h], v[0, h], SCALE, rows=rows)
+        zh = ofp8.quantize_head(q[0, h], k[0, h], v[0, h])
+        model = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows)
+        fl_cos, fl_ma = ofp8.cosine(model, truth), ofp8.max_abs(model, truth)
+        cos, ma = ofp8.cosine(got[i], truth), ofp8.max_abs(got[i], truth)
+        log(f"{name} head {h} vs truth: gpu cos={cos:.6f} max_abs={ma:.3e} | "
+            f"ideal-quantisation floor cos={fl_cos:.6f} max_abs={fl_ma:.3e}")
+        assert 1 - cos <= 1.5 * (1 - fl_cos) + 1e-5
+        assert ma <= 1.5 * fl_ma + 1e-3

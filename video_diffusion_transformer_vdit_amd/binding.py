@@ -1,0 +1,170 @@
+"""ctypes binding of libvdit_attn.so with the C ABI's names.
+
+Argument marshalling only: every step of the attention runs in the HIP
+library.  torch supplies device memory and the current HIP stream; nothing
+here computes on the CPU, and a missing library raises instead of falling
+back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvdit_attn.so")
+HEAD_DIM = 128
+FP8_BLOCK = 64
+DTYPE_BF16 = 0
+
+STATUS = {0: "VDIT_OK", 1: "VDIT_ERR_INVALID_ARG", 2: "VDIT_ERR_UNSUPPORTED", 3: "VDIT_ERR_HIP"}
+
+# exported symbol -> (restype, argtypes)
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "vdit_abi_version": (_I, []),
+    "vdit_status_str": (ctypes.c_char_p, [_I]),
+    "vdit_last_error": (ctypes.c_char_p, []),
+    "vdit_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "vdit_attn_quant_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _Z,
+                                 _I, _I, _I, _I, _P]),
+    "vdit_attn_quant_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "vdit_attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
+}
+
+_lib = None
+
+
+class VditError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load the library once and attach the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m video_diffusion_transformer_vdit_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        raise VditError(status, lib.vdit_last_error().decode() or lib.vdit_status_str(status).decode())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _shape4(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, S, D] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def vdit_attn_fwd(q, k, v, o=None, scale=None, stream=None):
+    """o = softmax(scale q k^T) v for bf16 [B, H, S, 128] tensors; returns o."""
+    import torch
+    B, H, S, D = _shape4(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if o is None:
+        o = torch.empty_like(q)
+    scale = D ** -0.5 if scale is None else float(scale)
+    lib = load()
+    check(lib.vdit_attn_fwd(_dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
+                            _dev(v, torch.bfloat16, "v"), _dev(o, torch.bfloat16, "o"),
+                            B, H, S, D, scale, DTYPE_BF16, _stream(stream)))
+    return o
+
+
+def quant_buffers(B, H, S, k_mean_blocks=None, device="cuda"):
+    """Allocate the pre-pass outputs and workspace (torch, on ``device``)."""
+    import torch
+    nb = -(-S // FP8_BLOCK)
+    kmb = nb if k_mean_blocks is None else int(k_mean_blocks)
+    lib = load()
+    ws = int(lib.vdit_attn_quant_fp8_workspace_size(B, H, S, HEAD_DIM, kmb))
+    if ws == 0:
+        raise ValueError("invalid shape or k_mean_blocks for the fp8 pre-pass")
+    f32 = dict(dtype=torch.float32, device=device)
+    u8 = dict(dtype=torch.uint8, device=device)
+    return {
+        "q8": torch.empty((B, H, S, HEAD_DIM), **u8),
+        "k8": torch.empty((B, H, S, HEAD_DIM), **u8),
+        "v8": torch.empty((B, H, S, HEAD_DIM), **u8),
+        "q_scale": torch.empty((B, H, nb), **f32),
+        "k_scale": torch.empty((B, H, nb), **f32),
+        "k_mean": torch.empty((B, H, kmb, HEAD_DIM), **f32),
+        "v_mean": torch.empty((B, H, HEAD_DIM), **f32),
+        "v_scale": torch.empty((B, H, HEAD_DIM), **f32),
+        "workspace": torch.empty(ws, **u8),
+    }
+
+
+def vdit_attn_quant_fp8(q, k, v, k_mean_blocks=None, out=None, stream=None):
+    """fp8 pre-pass on bf16 q, k, v; returns the dict of quant_buffers()."""
+    import torch
+    B, H, S, D = _shape4(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    z = quant_buffers(B, H, S, k_mean_blocks, q.device) if out is None else out
+    kmb = int(z["k_mean"].shape[2])
+    lib = load()
+    check(lib.vdit_attn_quant_fp8(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),
+        _dev(z["v8"], torch.uint8, "v8"), _dev(z["q_scale"], torch.float32, "q_scale"),
+        _dev(z["k_scale"], torch.float32, "k_scale"), _dev(z["k_mean"], torch.float32, "k_mean"),
+        kmb, _dev(z["v_mean"], torch.float32, "v_mean"), _dev(z["v_scale"], torch.float32, "v_scale"),
+        _dev(z["workspace"], torch.uint8, "workspace"), z["workspace"].numel(),
+        B, H, S, D, _stream(stream)))
+    return z
+
+
+def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None):
+    """fp8 attention on pre-pass outputs ``z`` (dict as from vdit_attn_quant_fp8);
+    returns bf16 o [B, H, S, 128]."""
+    import torch
+    B, H, S, D = _shape4(z["q8"])
+    if o is None:
+        o = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=z["q8"].device)
+    scale = D ** -0.5 if scale is None else float(scale)
+    kmb = int(z["k_mean"].shape[2])
+    lib = load()
+    check(lib.vdit_attn_fwd_fp8(
+        _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),
+        _dev(z["v8"], torch.uint8, "v8"), _dev(z["q_scale"], torch.float32, "q_scale"),
+        _dev(z["k_scale"], torch.float32, "k_scale"), _dev(z["k_mean"], torch.float32, "k_mean"),
+        kmb, _dev(z["v_mean"], torch.float32, "v_mean"), _dev(z["v_scale"], torch.float32, "v_scale"),
+        _dev(o, torch.bfloat16, "o"), B, H, S, D, scale, _stream(stream)))
+    return o

@@ -1,0 +1,156 @@
+// C ABI of libvdit_attn: argument validation, error reporting and dispatch to
+// the gfx950 kernels.  Every check runs before any HIP call, so the checks
+// can be exercised on a machine without a GPU.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/vdit_attn.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+vdit_status fail(vdit_status s, const char* fmt, const char* what) {
+  std::snprintf(g_last_error, sizeof(g_last_error), fmt, what);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, const void* b, size_t bytes_a, size_t bytes_b) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bytes_b && y < x + bytes_a;
+}
+
+// Shape checks shared by every entry point.
+vdit_status check_shape(int B, int H, int S, int D) {
+  if (B < 1 || H < 1 || S < 1) return fail(VDIT_ERR_INVALID_ARG, "%s", "B, H and S must be >= 1");
+  if (D != VDIT_HEAD_DIM) return fail(VDIT_ERR_UNSUPPORTED, "%s", "only D = 128 is supported");
+  // grid = B*H*ceil(S/128) workgroups must fit a 32-bit grid dimension, and
+  // per-head offsets are 64-bit.
+  const long long tiles = (long long)B * H * ((S + 127) / 128);
+  if (tiles > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL)
+    return fail(VDIT_ERR_UNSUPPORTED, "%s", "problem too large for one launch");
+  return VDIT_OK;
+}
+
+vdit_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(VDIT_ERR_INVALID_ARG, "null pointer: %s", name);
+  if (!aligned16(p)) return fail(VDIT_ERR_INVALID_ARG, "pointer not 16-byte aligned: %s", name);
+  return VDIT_OK;
+}
+
+vdit_status check_fptr(const void* p, const char* name) { return check_ptr(p, name); }
+
+vdit_status hip_result(hipError_t e) {
+  if (e == hipSuccess) {
+    g_last_error[0] = '\0';
+    return VDIT_OK;
+  }
+  return fail(VDIT_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+}
+
+bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
+
+#define VDIT_TRY(expr)                 \
+  do {                                 \
+    const vdit_status st_ = (expr);    \
+    if (st_ != VDIT_OK) return st_;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int vdit_abi_version(void) { return VDIT_ABI_VERSION; }
+
+const char* vdit_status_str(int status) {
+  switch (status) {
+    case VDIT_OK: return "ok";
+    case VDIT_ERR_INVALID_ARG: return "invalid argument";
+    case VDIT_ERR_UNSUPPORTED: return "unsupported argument";
+    case VDIT_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* vdit_last_error(void) { return g_last_error; }
+
+vdit_status vdit_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
+                          int S, int D, float scale, int dtype, void* stream) {
+  VDIT_TRY(check_ptr(q, "q"));
+  VDIT_TRY(check_ptr(k, "k"));
+  VDIT_TRY(check_ptr(v, "v"));
+  VDIT_TRY(check_ptr(o, "o"));
+  VDIT_TRY(check_shape(B, H, S, D));
+  if (!scale_ok(scale)) return fail(VDIT_ERR_INVALID_ARG, "%s", "scale must be finite and > 0");
+  if (dtype != VDIT_DTYPE_BF16) return fail(VDIT_ERR_UNSUPPORTED, "%s", "dtype must be VDIT_DTYPE_BF16");
+  const size_t bytes = (size_t)B * H * S * D * 2;
+  if (overlaps(o, q, bytes, bytes) || overlaps(o, k, bytes, bytes) || overlaps(o, v, bytes, bytes))
+    return fail(VDIT_ERR_INVALID_ARG, "%s", "o overlaps an input");
+  return hip_result(vdit::launch_attn_fwd_bf16(q, k, v, o, B, H, S, scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v, void* q8, void* k8,
+                                void* v8, float* q_scale, float* k_scale, float* k_mean,
+                                int k_mean_blocks, float* v_mean, float* v_scale, void* workspace,
+                                size_t workspace_bytes, int B, int H, int S, int D,
+                                void* stream) {
+  VDIT_TRY(check_ptr(q, "q"));
+  VDIT_TRY(check_ptr(k, "k"));
+  VDIT_TRY(check_ptr(v, "v"));
+  VDIT_TRY(check_ptr(q8, "q8"));
+  VDIT_TRY(check_ptr(k8, "k8"));
+  VDIT_TRY(check_ptr(v8, "v8"));
+  VDIT_TRY(check_fptr(q_scale, "q_scale"));
+  VDIT_TRY(check_fptr(k_scale, "k_scale"));
+  VDIT_TRY(check_fptr(k_mean, "k_mean"));
+  VDIT_TRY(check_fptr(v_mean, "v_mean"));
+  VDIT_TRY(check_fptr(v_scale, "v_scale"));
+  VDIT_TRY(check_ptr(workspace, "workspace"));
+  VDIT_TRY(check_shape(B, H, S, D));
+  const int nb = (S + VDIT_FP8_BLOCK - 1) / VDIT_FP8_BLOCK;
+  if (k_mean_blocks != 1 && k_mean_blocks != nb)
+    return fail(VDIT_ERR_UNSUPPORTED, "%s", "k_mean_blocks must be 1 or ceil(S/64)");
+  if (workspace_bytes < vdit::quant_fp8_workspace_bytes(B, H, S, k_mean_blocks))
+    return fail(VDIT_ERR_INVALID_ARG, "%s", "workspace too small");
+  return hip_result(vdit::launch_quant_fp8(q, k, v, q8, k8, v8, q_scale, k_scale, k_mean,
+                                           k_mean_blocks, v_mean, v_scale, workspace, B, H, S,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean_blocks) {
+  if (check_shape(B, H, S, D) != VDIT_OK) return 0;
+  const int nb = (S + VDIT_FP8_BLOCK - 1) / VDIT_FP8_BLOCK;
+  if (k_mean_blocks != 1 && k_mean_blocks != nb) return 0;
+  return vdit::quant_fp8_workspace_bytes(B, H, S, k_mean_blocks);
+}
+
+vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                              const float* q_scale, const float* k_scale, const float* k_mean,
+                              int k_mean_blocks, const float* v_mean, const float* v_scale,
+                              void* o, int B, int H, int S, int D, float scale, void* stream) {
+  VDIT_TRY(check_ptr(q8, "q8"));
+  VDIT_TRY(check_ptr(k8, "k8"));
+  VDIT_TRY(check_ptr(v8, "v8"));
+  VDIT_TRY(check_fptr(q_scale, "q_scale"));
+  VDIT_TRY(check_fptr(k_scale, "k_scale"));
+  VDIT_TRY(check_fptr(k_mean, "k_mean"));
+  VDIT_TRY(check_fptr(v_mean, "v_mean"));
+  VDIT_TRY(check_fptr(v_scale, "v_scale"));
+  VDIT_TRY(check_ptr(o, "o"));
+  VDIT_TRY(check_shape(B, H, S, D));
+  if (!scale_ok(scale)) return fail(VDIT_ERR_INVALID_ARG, "%s", "scale must be finite and > 0");
+  const int nb = (S + VDIT_FP8_BLOCK - 1) / VDIT_FP8_BLOCK;
+  if (k_mean_blocks != 1 && k_mean_blocks != nb)
+    return fail(VDIT_ERR_UNSUPPORTED, "%s", "k_mean_blocks must be 1 or ceil(S/64)");
+  return hip_result(vdit::launch_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks,
+                                              v_mean, v_scale, o, B, H, S, scale,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

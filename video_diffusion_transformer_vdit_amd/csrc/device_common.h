@@ -1,0 +1,49 @@
+// Device-side helpers shared by the gfx950 kernels of libvdit_attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vdit {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Workgroups are dealt round-robin to the 8 XCDs of an MI355X (block i runs
+// on XCD i % 8).  Renumber them so that each XCD receives one contiguous
+// range of logical tiles: tiles of one head then share that XCD's L2 while
+// they stream the same K/V tiles.  Bijective for any grid size.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int x = bid % kXcd;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  return x * q + min(x, r) + bid / kXcd;
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane (l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, nearest even
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace vdit

@@ -1,0 +1,25 @@
+// Internal launch wrappers of libvdit_attn (host side).  Arguments have been
+// validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace vdit {
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
+                                int B, int H, int S, float scale, hipStream_t stream);
+
+size_t quant_fp8_workspace_bytes(int B, int H, int S, int k_mean_blocks);
+
+hipError_t launch_quant_fp8(const void* q, const void* k, const void* v,
+                            void* q8, void* k8, void* v8, float* q_scale, float* k_scale,
+                            float* k_mean, int k_mean_blocks, float* v_mean, float* v_scale,
+                            void* workspace, int B, int H, int S, hipStream_t stream);
+
+hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                               const float* q_scale, const float* k_scale,
+                               const float* k_mean, int k_mean_blocks,
+                               const float* v_mean, const float* v_scale, void* o,
+                               int B, int H, int S, float scale, hipStream_t stream);
+
+}  // namespace vdit

@@ -1,0 +1,410 @@
+// fp8 pre-pass: quantise and smooth bf16 Q, K, V into E4M3 codes, scales and
+// means for the fp8 attention kernel.
+//
+// V-Smooth (VC-Attention article (aikraft.ru), section 02): subtract a mean,
+// quantise only the residual per channel in E4M3; the mean is added back in
+// the attention epilogue.  Q/K smoothing before the low-bit QK^T (section 01):
+// K loses the mean of each 64-token block (or one mean per head), Q and the
+// K residual get one E4M3 scale per 64-token block.  The article fuses its
+// pre-processing into one kernel (section 04); here it is three HBM-bound
+// launches because the V statistics span the whole sequence:
+//   1. per (b,h, 64-token block): Q codes + scale; K block mean, residual
+//      codes + scale (block mode) or K partial sums (global mode); V partial
+//      sum / min / max per channel  -> workspace
+//   2. per (b,h): reduce the V (and global K) partials -> v_mean, v_scale,
+//      1/scale (workspace), k_mean (global mode)
+//   3. per (b,h, block): V residual codes; K residual codes (global mode)
+//
+// Integer-valued decisions are taken in a stated precision so they can be
+// checked bit for bit: sums of bf16 values in fp64 (exact for these inputs),
+// mean = fp32(sum / n), residual = fp32(x - mean), scale = fp32(amax / 448)
+// and inv = fp32(448 / amax) from fp64 quotients (1 and 0 when amax = 0),
+// code = E4M3 round-to-nearest-even of clamp(fp32(r * inv), +-448).
+#include "device_common.h"
+#include "launchers.h"
+
+namespace vdit {
+namespace {
+
+constexpr int kBlock = 64;     // tokens per block
+constexpr int kThreads = 256;  // 16 row groups x 16 chunks of 8 channels
+
+// E4M3 (OCP E4M3FN) encoder, round to nearest even, for |x| <= 448.
+// Normal results: round the fp32 mantissa to 3 bits with an integer carry
+// and rebias the exponent from 127 to 7.  Below 2^-6 the grid is 2^-9.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a < 0x3c800000u) {  // |x| < 2^-6
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    code = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 8 bf16 (one 16-byte chunk) -> 8 floats
+__device__ __forceinline__ void unpack8(u32x4 w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p, bool ok) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+
+// 8 codes of f[0..7] * inv -> two packed dwords
+__device__ __forceinline__ u32x2 encode8(const float* f, float inv) {
+  u32x2 r;
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = e4m3_rne(clamp448(__fmul_rn(f[i], inv)));
+  r.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  r.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// max over the workgroup of a per-thread value (all threads get it)
+__device__ __forceinline__ float block_max(float x, float* red) {
+  x = wave_max(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ void scales_from_amax(float amax, float* scale, float* inv) {
+  if (amax == 0.0f) {
+    *scale = 1.0f;
+    *inv = 0.0f;
+  } else {
+    *scale = (float)((double)amax / 448.0);
+    *inv = (float)(448.0 / (double)amax);
+  }
+}
+
+struct Workspace {
+  double* v_sum;  // [BH][nb][D]
+  float* v_min;   // [BH][nb][D]
+  float* v_max;   // [BH][nb][D]
+  float* v_inv;   // [BH][D]
+  double* k_sum;  // [BH][nb][D] (global K mean only)
+};
+
+// Launch 1: one workgroup per (bh, block).
+__global__ __launch_bounds__(kThreads) void quant_blocks_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint8_t* __restrict__ Q8, uint8_t* __restrict__ K8, float* __restrict__ q_scale,
+    float* __restrict__ k_scale, float* __restrict__ k_mean, Workspace ws, int S, int nb,
+    int k_global) {
+  __shared__ double red_d[16][kHeadDim];
+  __shared__ float red_f[2][16][kHeadDim];
+  __shared__ float mean_s[kHeadDim];
+  __shared__ float red[4];
+
+  const int bh = blockIdx.x / nb;
+  const int blk = blockIdx.x - bh * nb;
+  const int tid = threadIdx.x;
+  const int c = tid & 15, rg = tid >> 4;
+  const int row0 = blk * kBlock;
+  const int nvalid = min(kBlock, S - row0);
+  const size_t head = (size_t)bh * S * kHeadDim;
+
+  float q[4][8], k[4][8], v[4][8];
+  bool ok[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = rg + 16 * p;
+    ok[p] = r < nvalid;
+    const size_t off = head + (size_t)(row0 + r) * kHeadDim + 8 * c;
+    unpack8(ld16(Q + off, ok[p]), q[p]);
+    unpack8(ld16(K + off, ok[p]), k[p]);
+    unpack8(ld16(V + off, ok[p]), v[p]);
+  }
+
+  // ---- V partial statistics over this block's valid rows ----
+  {
+    double s[8];
+    float mn[8], mx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s[i] = 0.0;
+      mn[i] = INFINITY;
+      mx[i] = -INFINITY;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (ok[p]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          s[i] += (double)v[p][i];
+          mn[i] = fminf(mn[i], v[p][i]);
+          mx[i] = fmaxf(mx[i], v[p][i]);
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      red_d[rg][8 * c + i] = s[i];
+      red_f[0][rg][8 * c + i] = mn[i];
+      red_f[1][rg][8 * c + i] = mx[i];
+    }
+    __syncthreads();
+    if (tid < kHeadDim) {
+      double ts = 0.0;
+      float tmn = INFINITY, tmx = -INFINITY;
+      for (int g = 0; g < 16; ++g) {
+        ts += red_d[g][tid];
+        tmn = fminf(tmn, red_f[0][g][tid]);
+        tmx = fmaxf(tmx, red_f[1][g][tid]);
+      }
+      const size_t o = ((size_t)bh * nb + blk) * kHeadDim + tid;
+      ws.v_sum[o] = ts;
+      ws.v_min[o] = tmn;
+      ws.v_max[o] = tmx;
+    }
+    __syncthreads();
+  }
+
+  // ---- K: block mean (block mode) or partial sums (global mode) ----
+  {
+    double s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = 0.0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (ok[p]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] += (double)k[p][i];
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red_d[rg][8 * c + i] = s[i];
+    __syncthreads();
+    if (tid < kHeadDim) {
+      double ts = 0.0;
+      for (int g = 0; g < 16; ++g) ts += red_d[g][tid];
+      if (k_global) {
+        ws.k_sum[((size_t)bh * nb + blk) * kHeadDim + tid] = ts;
+      } else {
+        const float m = (float)(ts / (double)nvalid);
+        mean_s[tid] = m;
+        k_mean[((size_t)bh * nb + blk) * kHeadDim + tid] = m;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- Q codes (no smoothing) ----
+  {
+    float a = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, ok[p] ? fabsf(q[p][i]) : 0.f);
+    const float amax = block_max(a, red);
+    float sc, inv;
+    scales_from_amax(amax, &sc, &inv);
+    if (tid == 0) q_scale[(size_t)bh * nb + blk] = sc;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (ok[p])
+        *reinterpret_cast<u32x2*>(Q8 + head + (size_t)(row0 + rg + 16 * p) * kHeadDim + 8 * c) =
+            encode8(q[p], inv);
+  }
+
+  // ---- K residual codes (block mode) ----
+  if (!k_global) {
+    float a = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        k[p][i] = __fsub_rn(k[p][i], mean_s[8 * c + i]);
+        a = fmaxf(a, ok[p] ? fabsf(k[p][i]) : 0.f);
+      }
+    const float amax = block_max(a, red);
+    float sc, inv;
+    scales_from_amax(amax, &sc, &inv);
+    if (tid == 0) k_scale[(size_t)bh * nb + blk] = sc;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (ok[p])
+        *reinterpret_cast<u32x2*>(K8 + head + (size_t)(row0 + rg + 16 * p) * kHeadDim + 8 * c) =
+            encode8(k[p], inv);
+  }
+}
+
+// Launch 2: one workgroup per bh; thread t < 128 owns channel t.
+__global__ __launch_bounds__(kThreads) void quant_reduce_kernel(
+    float* __restrict__ v_mean, float* __restrict__ v_scale, float* __restrict__ k_mean,
+    Workspace ws, int S, int nb, int k_global) {
+  __shared__ double rs[2][kHeadDim];
+  __shared__ double rk[2][kHeadDim];
+  __shared__ float rmn[2][kHeadDim], rmx[2][kHeadDim];
+  const int bh = blockIdx.x;
+  const int d = threadIdx.x & 127, part = threadIdx.x >> 7;
+  double s = 0.0, sk = 0.0;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int b = part; b < nb; b += 2) {
+    const size_t o = ((size_t)bh * nb + b) * kHeadDim + d;
+    s += ws.v_sum[o];
+    mn = fminf(mn, ws.v_min[o]);
+    mx = fmaxf(mx, ws.v_max[o]);
+    if (k_global) sk += ws.k_sum[o];
+  }
+  rs[part][d] = s;
+  rk[part][d] = sk;
+  rmn[part][d] = mn;
+  rmx[part][d] = mx;
+  __syncthreads();
+  if (part == 0) {
+    const float mean = (float)((rs[0][d] + rs[1][d]) / (double)S);
+    const float lo = fminf(rmn[0][d], rmn[1][d]);
+    const float hi = fmaxf(rmx[0][d], rmx[1][d]);
+    // fp32 subtraction is monotone, so this is max_j |fp32(v_j - mean)|
+    const float amax = fmaxf(fabsf(__fsub_rn(hi, mean)), fabsf(__fsub_rn(lo, mean)));
+    float sc, inv;
+    scales_from_amax(amax, &sc, &inv);
+    v_mean[(size_t)bh * kHeadDim + d] = mean;
+    v_scale[(size_t)bh * kHeadDim + d] = sc;
+    ws.v_inv[(size_t)bh * kHeadDim + d] = inv;
+    if (k_global) k_mean[(size_t)bh * kHeadDim + d] = (float)((rk[0][d] + rk[1][d]) / (double)S);
+  }
+}
+
+// Launch 3: one workgroup per (bh, block): V residual codes, and K residual
+// codes + scale when K uses one global mean.
+__global__ __launch_bounds__(kThreads) void quant_residual_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint8_t* __restrict__ K8,
+    uint8_t* __restrict__ V8, float* __restrict__ k_scale, const float* __restrict__ k_mean,
+    const float* __restrict__ v_mean, Workspace ws, int S, int nb, int k_global) {
+  __shared__ float red[4];
+  const int bh = blockIdx.x / nb;
+  const int blk = blockIdx.x - bh * nb;
+  const int tid = threadIdx.x;
+  const int c = tid & 15, rg = tid >> 4;
+  const int row0 = blk * kBlock;
+  const int nvalid = min(kBlock, S - row0);
+  const size_t head = (size_t)bh * S * kHeadDim;
+  float vm[8], vi[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    vm[i] = v_mean[(size_t)bh * kHeadDim + 8 * c + i];
+    vi[i] = ws.v_inv[(size_t)bh * kHeadDim + 8 * c + i];
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = rg + 16 * p;
+    if (r < nvalid) {
+      const size_t off = head + (size_t)(row0 + r) * kHeadDim + 8 * c;
+      float f[8];
+      unpack8(ld16(V + off, true), f);
+      uint32_t cd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cd[i] = e4m3_rne(clamp448(__fmul_rn(__fsub_rn(f[i], vm[i]), vi[i])));
+      u32x2 w;
+      w.x = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
+      w.y = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+      *reinterpret_cast<u32x2*>(V8 + off) = w;
+    }
+  }
+  if (k_global) {
+    float km[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) km[i] = k_mean[(size_t)bh * kHeadDim + 8 * c + i];
+    float k[4][8];
+    float a = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = rg + 16 * p;
+      const bool ok = r < nvalid;
+      unpack8(ld16(K + head + (size_t)(row0 + r) * kHeadDim + 8 * c, ok), k[p]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        k[p][i] = __fsub_rn(k[p][i], km[i]);
+        a = fmaxf(a, ok ? fabsf(k[p][i]) : 0.f);
+      }
+    }
+    const float amax = block_max(a, red);
+    float sc, inv;
+    scales_from_amax(amax, &sc, &inv);
+    if (tid == 0) k_scale[(size_t)bh * nb + blk] = sc;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (rg + 16 * p < nvalid)
+        *reinterpret_cast<u32x2*>(K8 + head + (size_t)(row0 + rg + 16 * p) * kHeadDim + 8 * c) =
+            encode8(k[p], inv);
+  }
+}
+
+Workspace carve(void* base, int BH, int nb, int k_global) {
+  const size_t n = (size_t)BH * nb * kHeadDim;
+  char* p = static_cast<char*>(base);
+  Workspace ws;
+  ws.v_sum = reinterpret_cast<double*>(p);
+  p += n * sizeof(double);
+  ws.k_sum = k_global ? reinterpret_cast<double*>(p) : nullptr;
+  if (k_global) p += n * sizeof(double);
+  ws.v_min = reinterpret_cast<float*>(p);
+  p += n * sizeof(float);
+  ws.v_max = reinterpret_cast<float*>(p);
+  p += n * sizeof(float);
+  ws.v_inv = reinterpret_cast<float*>(p);
+  return ws;
+}
+
+}  // namespace
+
+size_t quant_fp8_workspace_bytes(int B, int H, int S, int k_mean_blocks) {
+  const int nb = (S + kBlock - 1) / kBlock;
+  const int k_global = (k_mean_blocks == 1 && nb > 1) ? 1 : 0;
+  const size_t n = (size_t)B * H * nb * kHeadDim;
+  return n * sizeof(double) * (k_global ? 2 : 1) + n * sizeof(float) * 2 +
+         (size_t)B * H * kHeadDim * sizeof(float);
+}
+
+hipError_t launch_quant_fp8(const void* q, const void* k, const void* v, void* q8, void* k8,
+                            void* v8, float* q_scale, float* k_scale, float* k_mean,
+                            int k_mean_blocks, float* v_mean, float* v_scale, void* workspace,
+                            int B, int H, int S, hipStream_t stream) {
+  const int nb = (S + kBlock - 1) / kBlock;
+  const int BH = B * H;
+  // With a single block the block mean is the global mean.
+  const int k_global = (k_mean_blocks == 1 && nb > 1) ? 1 : 0;
+  const Workspace ws = carve(workspace, BH, nb, k_global);
+  const unsigned grid = (unsigned)((size_t)BH * nb);
+  hipLaunchKernelGGL(quant_blocks_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint8_t*>(q8),
+                     static_cast<uint8_t*>(k8), q_scale, k_scale, k_mean, ws, S, nb, k_global);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quant_reduce_kernel, dim3(BH), dim3(kThreads), 0, stream, v_mean, v_scale,
+                     k_mean, ws, S, nb, k_global);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quant_residual_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<uint8_t*>(k8), static_cast<uint8_t*>(v8), k_scale, k_mean, v_mean,
+                     ws, S, nb, k_global);
+  return hipGetLastError();
+}
+
+}  // namespace vdit
