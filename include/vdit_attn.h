@@ -65,7 +65,8 @@ const char* vdit_last_error(void);
  *   scale   : softmax scale (usually 1/sqrt(D)); finite and > 0.
  *   dtype   : VDIT_DTYPE_BF16.
  * Softmax and accumulation are fp32; P is rounded to bf16 before the P.V
- * product; O is rounded to bf16 (nearest even).  o may not alias q, k or v.
+ * product and the row sum adds those rounded weights; O is rounded to bf16
+ * (nearest even).  o may not alias q, k or v.
  */
 vdit_status vdit_attn_fwd(const void* q, const void* k, const void* v, void* o,
                           int B, int H, int S, int D, float scale, int dtype,
@@ -109,8 +110,9 @@ size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean
 /*
  * fp8 attention forward on the pre-pass outputs (same shapes as above).
  * Scores: s_ij = q_scale_b(i) k_scale_b(j) (q8_i . k8_j) + q_hat_i . k_mean_b(j)
- * (the second term restores a per-block K mean exactly; with k_mean_blocks = 1
- * it is a per-row constant and is dropped).  Softmax in the log2 domain with
+ * (the second term restores the K mean; it is kept even when k_mean_blocks = 1
+ * makes it constant along a row, because it moves the grid P is rounded on).
+ * Softmax in the log2 domain with
  * an integer running reference; P is quantised as E4M3(448 * p) for the fp8
  * P.V product while the row sum uses the fp32 p; the epilogue adds v_mean
  * back (VC-Attention article, section 02, Restore):

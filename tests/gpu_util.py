@@ -16,7 +16,7 @@ BF16_MEAN_REL = 2e-3
 # quantisation model, see test_parity_fp8.py), plus an L1 mean-rel bar.
 FP8_COS = 0.999
 FP8_MAX_ABS = 5e-2
-FP8_MODEL_MEAN_REL = 1e-2
+FP8_MODEL_MEAN_REL = 5e-3
 
 
 def log(msg):

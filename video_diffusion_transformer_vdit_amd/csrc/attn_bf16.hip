@@ -6,110 +6,189 @@
 // tiling the FLOPS article (sudonull.com, "Optymalizacje") credits with
 // removing the 75K x 75K matrix.
 //
-// Design (one workgroup = 4 waves = 128 queries; two workgroups per CU):
+// Design (one workgroup = 4 waves = 128 queries; two workgroups per CU, so
+// every SIMD runs two independent waves):
 //  * Each wave owns 32 queries.  Its Q slice stays in registers for the whole
 //    key loop as the B operand of v_mfma_f32_32x32x16_bf16.
 //  * Scores are produced transposed, S^T = K Q^T, so lane (q, half) holds one
 //    query and 16 keys of every 32-key block: row max / row sum are in-lane,
-//    plus one exchange with lane ^ 32 for the max.
-//  * K/V tiles of 64 keys are staged through registers into a double-buffered
-//    LDS ring (one barrier per tile).  K is stored row-major; V is stored
-//    transposed (V^T, keys contiguous) by a register transpose at staging
-//    time so that O^T += V^T P^T reads 16-byte A operands.  Inside every
-//    16-key chunk, key bits 2 and 3 are swapped in V^T so that the P^T
-//    operand is exactly the S^T accumulator registers in order.
+//    plus one v_permlane32_swap for the max.
+//  * K/V tiles of 64 keys go straight from global memory to LDS
+//    (global_load_lds_dwordx4, no register staging) into a two-deep ring; one
+//    barrier per tile.  Rows are 256 B with the 16-byte chunks XOR-swizzled
+//    (K: chunk ^ (row & 15); V: chunk ^ 4*(row & 3)) so that the K operand
+//    reads (ds_read_b128) and the transposing V reads (ds_read_b64_tr_b16,
+//    which hands each lane 4 keys of one channel) are free of bank conflicts.
+//  * Software pipeline: while the exponentials of tile j are computed, the
+//    MFMAs of S(j+1) = K(j+1) Q^T and of O^T += V(j)^T P(j)^T are in flight.
 //  * Online softmax in the log2 domain with an integer running reference
 //    m (ceil of the running maximum of scale*log2(e)*s): P = 2^(c s - m) <= 1,
 //    and the accumulator is rescaled (by an exact power of two) only in the
-//    rare tiles where some row's maximum exceeds its reference.
-//  * Row padding: keys >= S are zero-filled and scored -inf in the last tile;
-//    queries >= S are computed on zeros and not stored.
+//    rare tiles where some row's maximum exceeds its reference.  P is rounded
+//    to bf16 once; the row sum adds exactly those rounded weights.
+//  * Ragged tails: rows of the last K/V tile past S are read from row S-1
+//    (finite data), scored -inf, and so weigh exactly 0; queries >= S are
+//    computed on zeros and not stored.
 #include "device_common.h"
 #include "launchers.h"
 
 namespace vdit {
 namespace {
 
-constexpr int kBr = 128;                 // queries per workgroup
-constexpr int kBc = 64;                  // keys per K/V tile
-constexpr int kThreads = 256;            // 4 waves
-constexpr int kKStride = kHeadDim + 8;   // bf16 per K row in LDS (272 B)
-constexpr int kVStride = kBc + 8;        // bf16 per V^T row in LDS (144 B)
-constexpr int kKBuf = kBc * kKStride;
-constexpr int kVBuf = kHeadDim * kVStride;
+constexpr int kBr = 128;               // queries per workgroup
+constexpr int kBc = 64;                // keys per K/V tile
+constexpr int kThreads = 256;          // 4 waves
+constexpr int kRowBytes = kHeadDim * 2;
+constexpr int kTileBytes = kBc * kRowBytes;  // 16 KB
 
-struct Staged {
-  u32x4 k[4];
-  u32x4 v[4];
-};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
-__device__ __forceinline__ u32x4 load16(const uint16_t* p, bool ok) {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+__device__ __forceinline__ lds_void* lds_ptr(void* p) { return (lds_void*)p; }
+
+// 8 keys x 1 channel for the V^T operand: two transposing 64-bit reads.
+__device__ __forceinline__ bf16x8 read_v_operand(const char* p0, const char* p1) {
+  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  const s16x8_t v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-// Thread t stages K rows {p*16 + t/16} (p = 0..3), 16-byte chunk t%16, and V
-// rows 4*(t/16) .. +3 of the same chunk (all coalesced 16-byte loads).
-__device__ __forceinline__ void load_tile(Staged& st, const uint16_t* Kh, const uint16_t* Vh,
-                                          int key0, int S, int tid) {
-  const int c8 = (tid & 15) * 8;
-  const int r = tid >> 4;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int row = key0 + p * 16 + r;
-    st.k[p] = load16(Kh + (size_t)row * kHeadDim + c8, row < S);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = key0 + 4 * r + i;
-    st.v[i] = load16(Vh + (size_t)row * kHeadDim + c8, row < S);
-  }
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ void store_tile(const Staged& st, uint16_t* Ks, uint16_t* Vs, int tid) {
-  const int c = tid & 15;
-  const int g = tid >> 4;
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-    *reinterpret_cast<u32x4*>(Ks + (p * 16 + g) * kKStride + c * 8) = st.k[p];
-  // keys 4g..4g+3 land at position 16*(g>>2) + 8*(g&1) + 4*((g>>1)&1)
-  const int pos = 16 * (g >> 2) + 8 * (g & 1) + 4 * ((g >> 1) & 1);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    u32x2 lo, hi;
-    lo.x = __byte_perm(st.v[0][w], st.v[1][w], 0x5410);
-    lo.y = __byte_perm(st.v[2][w], st.v[3][w], 0x5410);
-    hi.x = __byte_perm(st.v[0][w], st.v[1][w], 0x7632);
-    hi.y = __byte_perm(st.v[2][w], st.v[3][w], 0x7632);
-    *reinterpret_cast<u32x2*>(Vs + (c * 8 + 2 * w) * kVStride + pos) = lo;
-    *reinterpret_cast<u32x2*>(Vs + (c * 8 + 2 * w + 1) * kVStride + pos) = hi;
-  }
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * kKBuf];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * kVBuf];
+  // Four separate LDS objects (not one indexed array): the compiler can then
+  // tell that a DMA into one buffer does not alias reads of the other, and
+  // does not wait for the in-flight tile before reading the current one.
+  __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[kTileBytes];
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const size_t base = (size_t)bh * S * kHeadDim;
-  const uint16_t* Qh = Q + base;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
+  const char* Kh = reinterpret_cast<const char*>(K + base);
+  const char* Vh = reinterpret_cast<const char*>(V + base);
   uint16_t* Oh = O + base;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qt * kBr + wave * 32 + col;
+  const int nkt = (S + kBc - 1) / kBc;
+  const bool tail = (S % kBc) != 0;
 
-  bf16x8 qf[8];
+  // ---- per-lane constant offsets ----
+  // Loads: wave w, load i covers tile rows 16w + 4i + lane/16; lane writes
+  // physical chunk lane%16 of its row, so it fetches the logical chunk that
+  // the swizzle maps there.
+  const int lrow0 = 16 * wave + (lane >> 4);   // + 4i
+  const int pchunk = lane & 15;
+  int kgo[4], vgo[4];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    qf[kk] = __builtin_bit_cast(bf16x8, load16(Qh + (size_t)qrow * kHeadDim + 16 * kk + 8 * half, qrow < S));
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow0 + 4 * i;
+    kgo[i] = r * kRowBytes + 16 * (pchunk ^ (r & 15));
+    vgo[i] = r * kRowBytes + 16 * (pchunk ^ (4 * (r & 3)));
+  }
+  // K operand: lane (key = 32kb + col, half), kk -> logical chunk 2kk + half
+  int koff[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * kRowBytes + 16 * ((2 * kk + half) ^ (col & 15));
+  // V operand: 16-lane group g = lane/16, s = lane%16 reads row
+  // 16kc + 8r + 4(g>>1) + s/4, channels 32mb + 16(g&1) + 4(s%4) .. +3.
+  const int g = lane >> 4, s16 = lane & 15;
+  const int vrow = 4 * (g >> 1) + (s16 >> 2);
+  const int vx = 2 * (g & 1) + ((s16 >> 1) & 1);
+  int voff[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+    voff[mb] = vrow * kRowBytes + 16 * (4 * (mb ^ (s16 >> 2)) + vx) + 8 * (s16 & 1);
+
+  auto issue_k = [&](int t, char* buf) {
+    const int key0 = t * kBc;
+    const char* src = Kh + (size_t)key0 * kRowBytes;
+    char* dst = buf + 16 * wave * kRowBytes;
+    if (tail && t == nkt - 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = lrow0 + 4 * i;
+        const int row = min(key0 + r, S - 1);
+        const int go = (row - key0) * kRowBytes + 16 * (pchunk ^ (r & 15));
+        __builtin_amdgcn_global_load_lds(src + go, lds_ptr(dst + i * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(src + kgo[i], lds_ptr(dst + i * 1024), 16, 0, 0);
+    }
+  };
+  auto issue_v = [&](int t, char* buf) {
+    const int key0 = t * kBc;
+    const char* src = Vh + (size_t)key0 * kRowBytes;
+    char* dst = buf + 16 * wave * kRowBytes;
+    if (tail && t == nkt - 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = lrow0 + 4 * i;
+        const int row = min(key0 + r, S - 1);
+        const int go = (row - key0) * kRowBytes + 16 * (pchunk ^ (4 * (r & 3)));
+        __builtin_amdgcn_global_load_lds(src + go, lds_ptr(dst + i * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(src + vgo[i], lds_ptr(dst + i * 1024), 16, 0, 0);
+    }
+  };
+
+  // ---- Q operand (registers for the whole loop) ----
+  bf16x8 qf[8];
+  {
+    const uint16_t* Qr = Q + base + (size_t)min(qrow, S - 1) * kHeadDim;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(Qr + 16 * kk + 8 * half);
+      if (qrow >= S) w = u32x4{0u, 0u, 0u, 0u};
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  auto qk = [&](const char* Kb, f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * kRowBytes + koff[kk]);
+        s[kb] = mfma32x32x16_bf16(a, qf[kk], s[kb]);
+      }
+  };
+  auto mask_tail = [&](int t, f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = t * kBc + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (key >= S) s[kb][i] = -INFINITY;
+      }
+  };
 
   f32x16 acc[4];
 #pragma unroll
@@ -119,47 +198,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   float m_ref = -INFINITY;  // integer-valued log2-domain reference
   float l = 0.f;            // this lane's share of the row sum
 
-  const int nkt = (S + kBc - 1) / kBc;
-  Staged st;
-  load_tile(st, Kh, Vh, 0, S, tid);
-  store_tile(st, lds_k, lds_v, tid);
-  __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) load_tile(st, Kh, Vh, (j + 1) * kBc, S, tid);
-    const uint16_t* Ks = lds_k + buf * kKBuf;
-    const uint16_t* Vs = lds_v + buf * kVBuf;
-
-    // S^T[key][query] for two 32-key blocks.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kb + col) * kKStride + 16 * kk + 8 * half);
-        s[kb] = mfma32x32x16_bf16(a, qf[kk], s[kb]);
-      }
-    }
-    if (j == nkt - 1 && (S % kBc) != 0) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j * kBc + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (key >= S) s[kb][i] = -INFINITY;
-        }
-    }
-
-    float mx = s[0][0];
+  // Row maximum of a score tile, reference update and (rare) rescale.
+  auto update_max = [&](const f32x16* s) {
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float mnew = mx * c;
+      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    const float mnew = max_halves(mx) * c;
     if (__ballot(mnew > m_ref) != 0ull) {
       const float mnext = mnew > m_ref ? ceilf(mnew) : m_ref;
       const float alpha = exp2_fast(m_ref - mnext);
@@ -170,46 +216,104 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
       m_ref = mnext;
     }
+  };
 
-    uint32_t pk[2][8];
+  // P = bf16(2^(c s - m)) packed in S^T register order; l += sum of P.
+  auto softmax_p = [&](const f32x16* s, uint32_t (*pk)[8]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         const float p0 = exp2_fast(fmaf(s[kb][2 * p], c, -m_ref));
         const float p1 = exp2_fast(fmaf(s[kb][2 * p + 1], c, -m_ref));
-        l += p0;
-        l += p1;
         pk[kb][p] = pack_bf16x2(p0, p1);
+        l = sum_bf16x2(pk[kb][p], l);
       }
+  };
 
-    // O^T[d][query] += V^T P^T over four 16-key chunks.
+  // O^T += V^T P^T over four 16-key chunks (keys 16kc + 4half + {0..3} and
+  // 16kc + 8 + 4half + {0..3}, matching the S^T register order of P).
+  auto pv = [&](const char* Vb, uint32_t (*pk)[8]) {
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int kb = kc >> 1, cc = kc & 1;
-      u32x4 pw = {pk[kb][4 * cc], pk[kb][4 * cc + 1], pk[kb][4 * cc + 2], pk[kb][4 * cc + 3]};
+      const u32x4 pw = {pk[kb][4 * cc], pk[kb][4 * cc + 1], pk[kb][4 * cc + 2], pk[kb][4 * cc + 3]};
       const bf16x8 b = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + (32 * mb + col) * kVStride + 16 * kc + 8 * half);
+        const char* p0 = Vb + (16 * kc) * kRowBytes + voff[mb];
+        const bf16x8 a = read_v_operand(p0, p0 + 8 * kRowBytes);
         acc[mb] = mfma32x32x16_bf16(a, b, acc[mb]);
       }
     }
+  };
 
-    if (j + 1 < nkt) store_tile(st, lds_k + (buf ^ 1) * kKBuf, lds_v + (buf ^ 1) * kVBuf, tid);
-    __syncthreads();
+  auto wait_loads_and_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // ---- prologue: K(0), V(0), K(1) in flight; S(0) ----
+  issue_k(0, lds_k0);
+  issue_v(0, lds_v0);
+  if (nkt > 1) issue_k(1, lds_k1);
+  wait_loads_and_sync();
+  f32x16 s_cur[2];
+  qk(lds_k0, s_cur);
+  if (tail && nkt == 1) mask_tail(0, s_cur);
+  update_max(s_cur);
+  // every wave has read lds_k0 before anyone refills it
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+
+  // One pipelined step for tile j (which has a successor): tile j+1's K is in
+  // k_next, tile j's V in v_cur; V(j+1) goes to v_fill and K(j+2) to k_fill.
+  auto step = [&](int j, const char* k_next, const char* v_cur, char* v_fill, char* k_fill) {
+    issue_v(j + 1, v_fill);
+    if (j + 2 < nkt) issue_k(j + 2, k_fill);
+    uint32_t pk[2][8];
+    softmax_p(s_cur, pk);
+    f32x16 s_next[2];
+    qk(k_next, s_next);
+    pv(v_cur, pk);
+    if (tail && j + 2 == nkt) mask_tail(j + 1, s_next);
+    update_max(s_next);
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
+    wait_loads_and_sync();
+  };
+
+  // ---- main loop, unrolled by two so every LDS buffer is named statically ----
+  int j = 0;
+  for (; j + 2 < nkt; j += 2) {
+    step(j, lds_k1, lds_v0, lds_v1, lds_k0);
+    step(j + 1, lds_k0, lds_v1, lds_v0, lds_k1);
+  }
+  if (j + 1 < nkt) {
+    step(j, lds_k1, lds_v0, lds_v1, lds_k0);
+    ++j;
   }
 
-  const float inv = 1.0f / (l + swap_halves(l));
+  // ---- last tile (j = nkt - 1) ----
+  {
+    uint32_t pk[2][8];
+    softmax_p(s_cur, pk);
+    if (j & 1)
+      pv(lds_v1, pk);
+    else
+      pv(lds_v0, pk);
+  }
+
+  const float inv = 1.0f / sum_halves(l);
   if (qrow < S) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int gq = 0; gq < 4; ++gq) {
         u32x2 w;
-        w.x = pack_bf16x2(acc[mb][4 * g] * inv, acc[mb][4 * g + 1] * inv);
-        w.y = pack_bf16x2(acc[mb][4 * g + 2] * inv, acc[mb][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(Oh + (size_t)qrow * kHeadDim + 32 * mb + 8 * g + 4 * half) = w;
+        w.x = pack_bf16x2(acc[mb][4 * gq] * inv, acc[mb][4 * gq + 1] * inv);
+        w.y = pack_bf16x2(acc[mb][4 * gq + 2] * inv, acc[mb][4 * gq + 3] * inv);
+        *reinterpret_cast<u32x2*>(Oh + (size_t)qrow * kHeadDim + 32 * mb + 8 * gq + 4 * half) = w;
       }
   }
 }

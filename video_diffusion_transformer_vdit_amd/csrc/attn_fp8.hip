@@ -9,10 +9,13 @@
 //
 // Scores of query i and key j (key block b = j / 64):
 //   s_ij = q_scale_i k_scale_b (q8_i . k8_j) + q_hat_i . k_mean_b
-// The second term restores a per-block K mean exactly.  It is computed for 32
-// blocks at a time by eight bf16 MFMAs (k_mean x q_hat, q_hat = bf16 of the
-// dequantised Q) and parked in LDS; with one global K mean it is a per-row
-// constant and is dropped (softmax is shift invariant).
+// The second term restores the K mean.  q_hat . k_mean = q_scale (dec(q8) .
+// k_mean) where dec(q8) is exact in bf16 and k_mean is split into a bf16 high
+// part and a bf16 residual, so two bf16 MFMAs per 16 channels give it to
+// about 2^-16 relative.  With one mean per 64-token block it is computed for
+// 32 blocks at a time and parked in LDS; with one global mean it is computed
+// once.  It is applied even when it is constant along a row: a constant shift
+// does not change the softmax but it does move the fp8 grid P is rounded on.
 // Softmax runs in the log2 domain with an integer running reference m
 // (the ceiling of the running row maximum): p = 2^(t - m) <= 1.  P is
 // quantised as E4M3(448 p) for the fp8 PV product; the row sum takes the fp32
@@ -120,7 +123,8 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
-template <bool kComp>
+// kBlockMean: one K mean per 64-token block (else one mean per head)
+template <bool kBlockMean>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
     const float* __restrict__ v_scale, uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2 * kKBuf];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * kVBuf];
-  __shared__ float lds_comp[kComp ? 4 : 1][kCompBlocks][32];
+  __shared__ float lds_comp[4][kCompBlocks][32];
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
@@ -157,20 +161,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
   // all 32 queries of a wave sit in one 64-token scale block
   const float qsc = q_scale[(size_t)bh * nb + min(qrow, S - 1) / kBc] * c;
 
-  // q_hat in bf16 as the B operand of the compensation MFMAs (lane: query col,
-  // channels 16kk + 8half .. +7).
+  // dec(q8) in bf16 (exact) as the B operand of the K-mean MFMAs (lane:
+  // query col, channels 16kk + 8half .. +7).
   bf16x8 qh[8];
-  if (kComp) {
-    const float qs = q_scale[(size_t)bh * nb + min(qrow, S - 1) / kBc];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const u32x2 w = ld8(Q8h + (size_t)qrow * kHeadDim + 16 * kk + 8 * half, qok);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qh[kk][e] = (__bf16)e4m3_value((w[e >> 2] >> (8 * (e & 3))) & 255u);
+  }
+  const int nbm = kBlockMean ? nb : 1;
+  const float* kmh = k_mean + (size_t)bh * nbm * kHeadDim;
+  // dec(q8_i) . k_mean_b for b = b0 .. b0+31 (clamped to the last block),
+  // written to this wave's LDS slots lds_comp[wave][b - b0][query].
+  auto kmean_batch = [&](int b0) {
+    f32x16 cm;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cm[i] = 0.f;
+    const float* km = kmh + (size_t)min(b0 + col, nbm - 1) * kHeadDim;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const u32x2 w = ld8(Q8h + (size_t)qrow * kHeadDim + 16 * kk + 8 * half, qok);
-      float f[8];
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half + 4);
+      bf16x8 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = e4m3_value((w[e >> 2] >> (8 * (e & 3))) & 255u) * qs;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qh[kk][e] = (__bf16)f[e];
+      for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? a0[e] : a1[e - 4];
+        hi[e] = (__bf16)x;
+        lo[e] = (__bf16)(x - (float)hi[e]);
+      }
+      cm = mfma32x32x16_bf16(hi, qh[kk], cm);
+      cm = mfma32x32x16_bf16(lo, qh[kk], cm);
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lds_comp[wave][8 * (i >> 2) + 4 * half + (i & 3)][col] = cm[i];
+  };
+  // Each wave reads only its own slots, after its own writes (LDS operations
+  // of one wave complete in order), so no barrier is needed around them.
+  float cb_global = 0.f;
+  if (!kBlockMean) {
+    kmean_batch(0);
+    cb_global = lds_comp[wave][0][col] * qsc;
   }
 
   f32x16 acc[4];
@@ -190,30 +221,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
 
   for (int j = 0; j < nkt; ++j) {
     const int buf = j & 1;
-    if (kComp && (j % kCompBlocks) == 0) {
-      // comp[m][q] = k_mean[j + m] . q_hat[q] for the next 32 blocks
-      f32x16 cm;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cm[i] = 0.f;
-      const int blk = j + col;
-      const float* km = k_mean + ((size_t)bh * nb + min(blk, nb - 1)) * kHeadDim;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half + 4);
-        bf16x8 a;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = (__bf16)a0[e];
-          a[4 + e] = (__bf16)a1[e];
-        }
-        cm = mfma32x32x16_bf16(a, qh[kk], cm);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) lds_comp[wave][8 * (i >> 2) + 4 * half + (i & 3)][col] = cm[i];
-      // each wave only reads its own slots; the writes above complete before
-      // the reads below within the wave (LDS ops of a wave are in order)
-    }
+    if (kBlockMean && (j % kCompBlocks) == 0) kmean_batch(j);
     if (j + 1 < nkt) load_tile(st, K8h, V8h, ksh, j + 1, S, tid);
     const uint8_t* Ks = lds_k + buf * kKBuf;
     const uint8_t* Vs = lds_v + buf * kVBuf;
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
     // t = a * dot + cb (log2 domain); a >= 0, so the row max of t is at the
     // row max of dot.
     const float a = qsc * ks_cur;
-    const float cb = kComp ? lds_comp[wave][j % kCompBlocks][col] * c : 0.f;
+    const float cb = kBlockMean ? lds_comp[wave][j % kCompBlocks][col] * qsc : cb_global;
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -326,13 +334,13 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
   const int n_qtiles = (S + kBr - 1) / kBr;
   const unsigned blocks = (unsigned)((long long)B * H * n_qtiles);
   const int nb = (S + kBc - 1) / kBc;
-  const bool comp = k_mean_blocks == nb && nb > 1;
+  const bool block_mean = k_mean_blocks == nb && nb > 1;
   const uint8_t* q = static_cast<const uint8_t*>(q8);
   const uint8_t* k = static_cast<const uint8_t*>(k8);
   const uint8_t* v = static_cast<const uint8_t*>(v8);
   uint16_t* out = static_cast<uint16_t*>(o);
   const float c = scale * kLog2e;
-  if (comp)
+  if (block_mean)
     hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, q, k, v,
                        q_scale, k_scale, k_mean, v_mean, v_scale, out, S, n_qtiles, c);
   else

@@ -16,6 +16,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kHeadDim = 128;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -44,6 +46,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2 v = {a, b};
   bf16x2 r = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, nearest even
   return __builtin_bit_cast(uint32_t, r);
+}
+
+// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1))
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
 }
 
 }  // namespace vdit
