@@ -59,6 +59,49 @@ def time_launches(fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "video_diffusion_transformer_vdit_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_kernel__wan2.1-14b-720p__hbm_traffic.txt")
+
+
+def source_sha256(path=KERNEL_SOURCE):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the bf16 kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration);
+    None when absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, val = line.partition(":")
+                vals[key.strip()] = val.strip()
+    if vals.get("source_sha256") != source_sha256():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def calibration_copy(n_bytes=1 << 31, reps=3):
+    """Plain device-to-device copy of a known size, for scaling FETCH_SIZE /
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    x = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    x.fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n_bytes, "reps": reps}), flush=True)
+
+
 def cpu_baseline(w, q, k, v, scale, seconds):
     """fp64 oracle (as it stands) on head 0, 256-row chunks until `seconds`
     have elapsed; rate scaled to TFLOP/s of the same attention arithmetic."""
@@ -100,6 +143,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a 2 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -111,6 +156,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calib_copy:
+        calibration_copy()
+        return
     binding.load()
 
     w = inputs.get_workload(args.workload)
@@ -149,7 +197,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if w.name == HEADLINE else None,
             "algorithmic_flop_per_launch": w.flop,
             "algorithmic_bytes_per_launch": 4 * w.B * w.H * w.S * w.D * 2,
         },

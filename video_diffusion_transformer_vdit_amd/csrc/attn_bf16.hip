@@ -6,8 +6,8 @@
 // tiling the FLOPS article (sudonull.com, "Optymalizacje") credits with
 // removing the 75K x 75K matrix.
 //
-// Design (one workgroup = 4 waves = 128 queries; two workgroups per CU, so
-// every SIMD runs two independent waves):
+// Design (one workgroup = 8 waves = 256 queries, one workgroup per CU, so
+// every SIMD runs two waves that share each K/V tile in LDS):
 //  * Each wave owns 32 queries.  Its Q slice stays in registers for the whole
 //    key loop as the B operand of v_mfma_f32_32x32x16_bf16.
 //  * Scores are produced transposed, S^T = K Q^T, so lane (q, half) holds one
@@ -15,10 +15,12 @@
 //    plus one v_permlane32_swap for the max.
 //  * K/V tiles of 64 keys go straight from global memory to LDS
 //    (global_load_lds_dwordx4, no register staging) into a two-deep ring; one
-//    barrier per tile.  Rows are 256 B with the 16-byte chunks XOR-swizzled
-//    (K: chunk ^ (row & 15); V: chunk ^ 4*(row & 3)) so that the K operand
-//    reads (ds_read_b128) and the transposing V reads (ds_read_b64_tr_b16,
-//    which hands each lane 4 keys of one channel) are free of bank conflicts.
+//    barrier per tile.  K is stored chunk-major ([16-byte chunk][key]), so the
+//    K operand of every MFMA is one 16-byte read at a linear offset and
+//    consecutive lanes read consecutive bytes.  V is stored row-major with
+//    its 16-byte chunks XOR-swizzled (chunk ^ 4*(row & 3)) and read with
+//    ds_read_b64_tr_b16, which hands each lane 4 keys of one channel; both
+//    reads are free of bank conflicts.
 //  * Software pipeline: while the exponentials of tile j are computed, the
 //    MFMAs of S(j+1) = K(j+1) Q^T and of O^T += V(j)^T P(j)^T are in flight.
 //  * Online softmax in the log2 domain with an integer running reference
@@ -35,9 +37,11 @@
 namespace vdit {
 namespace {
 
-constexpr int kBr = 128;               // queries per workgroup
+constexpr int kWaves = 8;
+constexpr int kBr = 32 * kWaves;       // queries per workgroup
 constexpr int kBc = 64;                // keys per K/V tile
-constexpr int kThreads = 256;          // 4 waves
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLoadsPerWave = 16 / kWaves;  // 1 KB DMA loads per wave per tile
 constexpr int kRowBytes = kHeadDim * 2;
 constexpr int kTileBytes = kBc * kRowBytes;  // 16 KB
 
@@ -64,7 +68,7 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
   // Four separate LDS objects (not one indexed array): the compiler can then
@@ -91,22 +95,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const bool tail = (S % kBc) != 0;
 
   // ---- per-lane constant offsets ----
-  // Loads: wave w, load i covers tile rows 16w + 4i + lane/16; lane writes
+  // V loads: wave w, load i covers tile rows 8w + 4i + lane/16; lane writes
   // physical chunk lane%16 of its row, so it fetches the logical chunk that
-  // the swizzle maps there.
-  const int lrow0 = 16 * wave + (lane >> 4);   // + 4i
+  // the swizzle maps there.  K loads: load i of wave w fills chunk row
+  // c = 2w + i (1 KB) with chunk c of all 64 keys (lane = key).
+  const int lrow0 = 4 * kLoadsPerWave * wave + (lane >> 4);   // + 4i
   const int pchunk = lane & 15;
-  int kgo[4], vgo[4];
+  int kgo[kLoadsPerWave], vgo[kLoadsPerWave];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kLoadsPerWave; ++i) {
     const int r = lrow0 + 4 * i;
-    kgo[i] = r * kRowBytes + 16 * (pchunk ^ (r & 15));
+    kgo[i] = lane * kRowBytes + 16 * (kLoadsPerWave * wave + i);
     vgo[i] = r * kRowBytes + 16 * (pchunk ^ (4 * (r & 3)));
   }
-  // K operand: lane (key = 32kb + col, half), kk -> logical chunk 2kk + half
-  int koff[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * kRowBytes + 16 * ((2 * kk + half) ^ (col & 15));
+  // K operand: lane (key = 32kb + col, half) reads chunk 2kk + half of its key
+  const int kbase = half * 1024 + col * 16;
   // V operand: 16-lane group g = lane/16, s = lane%16 reads row
   // 16kc + 8r + 4(g>>1) + s/4, channels 32mb + 16(g&1) + 4(s%4) .. +3.
   const int g = lane >> 4, s16 = lane & 15;
@@ -120,28 +123,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   auto issue_k = [&](int t, char* buf) {
     const int key0 = t * kBc;
     const char* src = Kh + (size_t)key0 * kRowBytes;
-    char* dst = buf + 16 * wave * kRowBytes;
+    char* dst = buf + 4 * kLoadsPerWave * wave * kRowBytes;
     if (tail && t == nkt - 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = lrow0 + 4 * i;
-        const int row = min(key0 + r, S - 1);
-        const int go = (row - key0) * kRowBytes + 16 * (pchunk ^ (r & 15));
+      for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int row = min(key0 + lane, S - 1);
+        const int go = (row - key0) * kRowBytes + 16 * (kLoadsPerWave * wave + i);
         __builtin_amdgcn_global_load_lds(src + go, lds_ptr(dst + i * 1024), 16, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kLoadsPerWave; ++i)
         __builtin_amdgcn_global_load_lds(src + kgo[i], lds_ptr(dst + i * 1024), 16, 0, 0);
     }
   };
   auto issue_v = [&](int t, char* buf) {
     const int key0 = t * kBc;
     const char* src = Vh + (size_t)key0 * kRowBytes;
-    char* dst = buf + 16 * wave * kRowBytes;
+    char* dst = buf + 4 * kLoadsPerWave * wave * kRowBytes;
     if (tail && t == nkt - 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kLoadsPerWave; ++i) {
         const int r = lrow0 + 4 * i;
         const int row = min(key0 + r, S - 1);
         const int go = (row - key0) * kRowBytes + 16 * (pchunk ^ (4 * (r & 3)));
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kLoadsPerWave; ++i)
         __builtin_amdgcn_global_load_lds(src + vgo[i], lds_ptr(dst + i * 1024), 16, 0, 0);
     }
   };
@@ -176,11 +178,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * kRowBytes + koff[kk]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + 2048 * kk + 512 * kb + kbase);
         s[kb] = mfma32x32x16_bf16(a, qf[kk], s[kb]);
       }
   };
   auto mask_tail = [&](int t, f32x16* s) {
+    // keeps the compiler from turning this once-per-workgroup branch into
+    // selects executed on every tile
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -196,20 +201,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
   float m_ref = -INFINITY;  // integer-valued log2-domain reference
-  float l = 0.f;            // this lane's share of the row sum
+  // this lane's share of the row sum, in four independent partial sums so
+  // that the additions do not form one long dependency chain
+  float l4[4] = {0.f, 0.f, 0.f, 0.f};
 
   // Row maximum of a score tile, reference update and (rare) rescale.
   auto update_max = [&](const f32x16* s) {
-    float mx = fmaxf(s[0][0], s[0][1]);
+    // balanced tree over the 32 scores (depth 4 instead of a chain of 16)
+    float t8[8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    for (int u = 0; u < 8; ++u)
+      t8[u] = fmaxf(fmaxf(s[u >> 2][4 * (u & 3)], s[u >> 2][4 * (u & 3) + 1]),
+                    fmaxf(s[u >> 2][4 * (u & 3) + 2], s[u >> 2][4 * (u & 3) + 3]));
+    const float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
+                           fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
     const float mnew = max_halves(mx) * c;
     if (__ballot(mnew > m_ref) != 0ull) {
+      // rare: keep it a real branch rather than 64 multiplies per tile
+      asm volatile("" ::: "memory");
       const float mnext = mnew > m_ref ? ceilf(mnew) : m_ref;
       const float alpha = exp2_fast(m_ref - mnext);
-      l *= alpha;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) l4[u] *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -227,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         const float p0 = exp2_fast(fmaf(s[kb][2 * p], c, -m_ref));
         const float p1 = exp2_fast(fmaf(s[kb][2 * p + 1], c, -m_ref));
         pk[kb][p] = pack_bf16x2(p0, p1);
-        l = sum_bf16x2(pk[kb][p], l);
+        l4[p & 3] = sum_bf16x2(pk[kb][p], l4[p & 3]);
       }
   };
 
@@ -268,43 +281,51 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
   // One pipelined step for tile j (which has a successor): tile j+1's K is in
   // k_next, tile j's V in v_cur; V(j+1) goes to v_fill and K(j+2) to k_fill.
-  auto step = [&](int j, const char* k_next, const char* v_cur, char* v_fill, char* k_fill) {
+  // s_in holds S(j); S(j+1) is written to s_out (the two register sets swap
+  // roles from one step to the next, so nothing is copied).
+  auto step = [&](int j, const char* k_next, const char* v_cur, char* v_fill, char* k_fill,
+                  f32x16* s_in, f32x16* s_out) {
     issue_v(j + 1, v_fill);
     if (j + 2 < nkt) issue_k(j + 2, k_fill);
     uint32_t pk[2][8];
-    softmax_p(s_cur, pk);
-    f32x16 s_next[2];
-    qk(k_next, s_next);
+    softmax_p(s_in, pk);
+    qk(k_next, s_out);
     pv(v_cur, pk);
-    if (tail && j + 2 == nkt) mask_tail(j + 1, s_next);
-    update_max(s_next);
-    s_cur[0] = s_next[0];
-    s_cur[1] = s_next[1];
+    if (tail && j + 2 == nkt) mask_tail(j + 1, s_out);
+    update_max(s_out);
     wait_loads_and_sync();
   };
 
-  // ---- main loop, unrolled by two so every LDS buffer is named statically ----
+  // ---- main loop, unrolled by two so every LDS buffer and score register
+  // set is named statically ----
+  f32x16 s_alt[2];
   int j = 0;
   for (; j + 2 < nkt; j += 2) {
-    step(j, lds_k1, lds_v0, lds_v1, lds_k0);
-    step(j + 1, lds_k0, lds_v1, lds_v0, lds_k1);
+    step(j, lds_k1, lds_v0, lds_v1, lds_k0, s_cur, s_alt);
+    step(j + 1, lds_k0, lds_v1, lds_v0, lds_k1, s_alt, s_cur);
   }
+  bool in_alt = false;
   if (j + 1 < nkt) {
-    step(j, lds_k1, lds_v0, lds_v1, lds_k0);
+    step(j, lds_k1, lds_v0, lds_v1, lds_k0, s_cur, s_alt);
+    in_alt = true;
     ++j;
   }
 
-  // ---- last tile (j = nkt - 1) ----
-  {
+  // ---- last tile (j = nkt - 1); every register set is named statically ----
+  auto last_tile = [&](const f32x16* s_last) {
     uint32_t pk[2][8];
-    softmax_p(s_cur, pk);
+    softmax_p(s_last, pk);
     if (j & 1)
       pv(lds_v1, pk);
     else
       pv(lds_v0, pk);
-  }
+  };
+  if (in_alt)
+    last_tile(s_alt);
+  else
+    last_tile(s_cur);
 
-  const float inv = 1.0f / sum_halves(l);
+  const float inv = 1.0f / sum_halves((l4[0] + l4[1]) + (l4[2] + l4[3]));
   if (qrow < S) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
