@@ -13,16 +13,20 @@
 //  * Scores are produced transposed, S^T = K Q^T, so lane (q, half) holds one
 //    query and 16 keys of every 32-key block: row max / row sum are in-lane,
 //    plus one v_permlane32_swap for the max.
-//  * K/V tiles of 64 keys go straight from global memory to LDS
-//    (global_load_lds_dwordx4, no register staging) into a two-deep ring; one
-//    barrier per tile.  K is stored chunk-major ([16-byte chunk][key]), so the
-//    K operand of every MFMA is one 16-byte read at a linear offset and
-//    consecutive lanes read consecutive bytes.  V is stored row-major with
-//    its 16-byte chunks XOR-swizzled (chunk ^ 4*(row & 3)) and read with
-//    ds_read_b64_tr_b16, which hands each lane 4 keys of one channel; both
-//    reads are free of bank conflicts.
-//  * Software pipeline: while the exponentials of tile j are computed, the
-//    MFMAs of S(j+1) = K(j+1) Q^T and of O^T += V(j)^T P(j)^T are in flight.
+//  * Ping-pong between the two waves of a SIMD.  Per 64-key tile a wave runs
+//    an exponential phase (reference update, P = 2^(c s - m), VALU) and a
+//    matrix phase (S of the next tile and O += P V, MFMA).  Waves 0-3 and
+//    4-7 run one phase apart, so each SIMD overlaps one wave's exponentials
+//    with the other wave's MFMAs; a workgroup barrier ends every phase.
+//    Within a matrix phase every LDS operand read is issued six MFMAs ahead
+//    of its use.
+//  * K/V tiles go straight from global memory to LDS (global_load_lds_dwordx4,
+//    no register staging) into three-deep rings.  K is stored chunk-major
+//    ([16-byte chunk][key]), so the K operand of every MFMA is one 16-byte
+//    read at a linear offset and consecutive lanes read consecutive bytes.  V
+//    is stored row-major with its 16-byte chunks XOR-swizzled
+//    (chunk ^ 4*(row & 3)) and read with ds_read_b64_tr_b16, which hands each
+//    lane 4 keys of one channel; both reads are free of bank conflicts.
 //  * Online softmax in the log2 domain with an integer running reference
 //    m (ceil of the running maximum of scale*log2(e)*s): P = 2^(c s - m) <= 1,
 //    and the accumulator is rescaled (by an exact power of two) only in the
@@ -38,10 +42,10 @@ namespace vdit {
 namespace {
 
 constexpr int kWaves = 8;
-constexpr int kBr = 32 * kWaves;       // queries per workgroup
-constexpr int kBc = 64;                // keys per K/V tile
+constexpr int kBr = 32 * kWaves;        // 256 queries per workgroup
+constexpr int kBc = 64;                 // keys per K/V tile
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLoadsPerWave = 16 / kWaves;  // 1 KB DMA loads per wave per tile
+constexpr int kLoadsPerWave = 16 / kWaves;  // 1 KB DMA loads per wave per tile and tensor
 constexpr int kRowBytes = kHeadDim * 2;
 constexpr int kTileBytes = kBc * kRowBytes;  // 16 KB
 
@@ -49,6 +53,36 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 __device__ __forceinline__ lds_void* lds_ptr(void* p) { return (lds_void*)p; }
+
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// global_load_lds_dwordx4 written out: 16 bytes per lane from gbase + voff
+// to LDS address m0 + 16 * lane.  Issued through asm so that the compiler
+// does not track the LDS write (it cannot tell the K/V buffers apart and
+// would wait for every DMA before each LDS read); the kernel waits for these
+// loads itself (s_waitcnt vmcnt + s_barrier) before any wave reads the
+// buffer.  M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(uniform_ptr(gbase))
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
+}
 
 // 8 keys x 1 channel for the V^T operand: two transposing 64-bit reads.
 __device__ __forceinline__ bf16x8 read_v_operand(const char* p0, const char* p1) {
@@ -68,16 +102,17 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
+
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
-  // Four separate LDS objects (not one indexed array): the compiler can then
-  // tell that a DMA into one buffer does not alias reads of the other, and
-  // does not wait for the in-flight tile before reading the current one.
+  // three-deep rings of K and V tiles, one LDS object per buffer
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v2[kTileBytes];
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
@@ -88,7 +123,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
   uint16_t* Oh = O + base;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qt * kBr + wave * 32 + col;
   const int nkt = (S + kBc - 1) / kBc;
@@ -99,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
   // physical chunk lane%16 of its row, so it fetches the logical chunk that
   // the swizzle maps there.  K loads: load i of wave w fills chunk row
   // c = 2w + i (1 KB) with chunk c of all 64 keys (lane = key).
-  const int lrow0 = 4 * kLoadsPerWave * wave + (lane >> 4);   // + 4i
+  const int lrow0 = 4 * kLoadsPerWave * wave + (lane >> 4);  // + 4i
   const int pchunk = lane & 15;
   int kgo[kLoadsPerWave], vgo[kLoadsPerWave];
 #pragma unroll
@@ -120,39 +155,40 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
   for (int mb = 0; mb < 4; ++mb)
     voff[mb] = vrow * kRowBytes + 16 * (4 * (mb ^ (s16 >> 2)) + vx) + 8 * (s16 & 1);
 
-  auto issue_k = [&](int t, char* buf) {
+  const uint32_t wslice = (uint32_t)wave * (4 * kLoadsPerWave * kRowBytes);
+  auto issue_k = [&](int t, const void* buf) __attribute__((always_inline)) {
+    t = min(t, nkt - 1);  // past the end: reload the last tile into a free buffer
     const int key0 = t * kBc;
     const char* src = Kh + (size_t)key0 * kRowBytes;
-    char* dst = buf + 4 * kLoadsPerWave * wave * kRowBytes;
+    const uint32_t dst = lds_addr(buf) + wslice;
     if (tail && t == nkt - 1) {
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int row = min(key0 + lane, S - 1);
         const int go = (row - key0) * kRowBytes + 16 * (kLoadsPerWave * wave + i);
-        __builtin_amdgcn_global_load_lds(src + go, lds_ptr(dst + i * 1024), 16, 0, 0);
+        dma16(src, (uint32_t)go, dst + i * 1024);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kLoadsPerWave; ++i)
-        __builtin_amdgcn_global_load_lds(src + kgo[i], lds_ptr(dst + i * 1024), 16, 0, 0);
+      for (int i = 0; i < kLoadsPerWave; ++i) dma16(src, (uint32_t)kgo[i], dst + i * 1024);
     }
   };
-  auto issue_v = [&](int t, char* buf) {
+  auto issue_v = [&](int t, const void* buf) __attribute__((always_inline)) {
+    t = min(t, nkt - 1);
     const int key0 = t * kBc;
     const char* src = Vh + (size_t)key0 * kRowBytes;
-    char* dst = buf + 4 * kLoadsPerWave * wave * kRowBytes;
+    const uint32_t dst = lds_addr(buf) + wslice;
     if (tail && t == nkt - 1) {
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int r = lrow0 + 4 * i;
         const int row = min(key0 + r, S - 1);
         const int go = (row - key0) * kRowBytes + 16 * (pchunk ^ (4 * (r & 3)));
-        __builtin_amdgcn_global_load_lds(src + go, lds_ptr(dst + i * 1024), 16, 0, 0);
+        dma16(src, (uint32_t)go, dst + i * 1024);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kLoadsPerWave; ++i)
-        __builtin_amdgcn_global_load_lds(src + vgo[i], lds_ptr(dst + i * 1024), 16, 0, 0);
+      for (int i = 0; i < kLoadsPerWave; ++i) dma16(src, (uint32_t)vgo[i], dst + i * 1024);
     }
   };
 
@@ -168,12 +204,12 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
     }
   }
 
-  auto qk = [&](const char* Kb, f32x16* s) {
+  f32x16 s[2];  // S^T of one tile: key block kb, lane (q, half): keys 32kb + 8(i/4) + 4half + i%4
+  auto qk = [&](const char* Kb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-    }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
@@ -182,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
         s[kb] = mfma32x32x16_bf16(a, qf[kk], s[kb]);
       }
   };
-  auto mask_tail = [&](int t, f32x16* s) {
+  auto mask_tail = [&](int t) __attribute__((always_inline)) {
     // keeps the compiler from turning this once-per-workgroup branch into
     // selects executed on every tile
     asm volatile("" ::: "memory");
@@ -201,38 +237,35 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
   float m_ref = -INFINITY;  // integer-valued log2-domain reference
-  // this lane's share of the row sum, in four independent partial sums so
-  // that the additions do not form one long dependency chain
   float l4[4] = {0.f, 0.f, 0.f, 0.f};
 
-  // Row maximum of a score tile, reference update and (rare) rescale.
-  auto update_max = [&](const f32x16* s) {
-    // balanced tree over the 32 scores (depth 4 instead of a chain of 16)
+  // Reference update and (rare) rescale.  In the common case only the
+  // lane-local maximum is formed and compared with the reference.
+  auto update_max = [&]() __attribute__((always_inline)) {
     float t8[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       t8[u] = fmaxf(fmaxf(s[u >> 2][4 * (u & 3)], s[u >> 2][4 * (u & 3) + 1]),
                     fmaxf(s[u >> 2][4 * (u & 3) + 2], s[u >> 2][4 * (u & 3) + 3]));
     const float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
-                           fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
-    const float mnew = max_halves(mx) * c;
-    if (__ballot(mnew > m_ref) != 0ull) {
+                           fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7]))) * c;
+    if (__ballot(mx > m_ref) != 0ull) {
       // rare: keep it a real branch rather than 64 multiplies per tile
       asm volatile("" ::: "memory");
-      const float mnext = mnew > m_ref ? ceilf(mnew) : m_ref;
+      const float mq = max_halves(mx);
+      const float mnext = mq > m_ref ? ceilf(mq) : m_ref;
       const float alpha = exp2_fast(m_ref - mnext);
 #pragma unroll
       for (int u = 0; u < 4; ++u) l4[u] *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
+      for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
       m_ref = mnext;
     }
   };
 
   // P = bf16(2^(c s - m)) packed in S^T register order; l += sum of P.
-  auto softmax_p = [&](const f32x16* s, uint32_t (*pk)[8]) {
+  uint32_t pk[2][8];
+  auto softmax_p = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -246,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
 
   // O^T += V^T P^T over four 16-key chunks (keys 16kc + 4half + {0..3} and
   // 16kc + 8 + 4half + {0..3}, matching the S^T register order of P).
-  auto pv = [&](const char* Vb, uint32_t (*pk)[8]) {
+  auto pv = [&](const char* Vb) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int kb = kc >> 1, cc = kc & 1;
@@ -261,69 +294,104 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_fwd_bf16_kernel(
     }
   };
 
-  auto wait_loads_and_sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  // workgroup barrier that the compiler moves no memory access across
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
-  // ---- prologue: K(0), V(0), K(1) in flight; S(0) ----
+  // ---- two wave groups in ping-pong ----
+  // Waves 0-3 (group A, one per SIMD) and 4-7 (group B) run the same
+  // sequence of phases, B one phase behind A, so that while one wave of a
+  // SIMD is in its exponential phase (VALU) the other is in its matrix phase
+  // (MFMA).  Phase P1(t): reference update and P = 2^(c s - m) of tile t;
+  // phase P2(t): S of tile t+1 (QK^T) and O += P(t) V(t).  A barrier ends
+  // every phase.  K and V tiles live in three-deep rings; at the start of
+  // P2(t) every wave issues its share of K(t+3) and V(t+2), into the
+  // buffers of K(t) and V(t-1), which both groups have finished reading by
+  // then.  Each wave waits for all but its newest batch of loads before
+  // every barrier, so a load has at least two phases to land before the
+  // barrier that precedes its first use.
+  const bool group_a = wave < 4;
+  auto phase1 = [&]() __attribute__((always_inline)) {
+    update_max();
+    softmax_p();
+    // consume P here: otherwise the exponentials are moved to their use
+    // after the barrier, into the MFMA phase
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      asm volatile("" ::"v"(pk[kb][0]), "v"(pk[kb][1]), "v"(pk[kb][2]), "v"(pk[kb][3]), "v"(pk[kb][4]),
+                   "v"(pk[kb][5]), "v"(pk[kb][6]), "v"(pk[kb][7]));
+    __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4): all but the newest batch
+    __builtin_amdgcn_sched_barrier(0);
+    barrier();
+  };
+  auto phase2 = [&](int t, const char* kn, const char* vc, const void* kfill, const void* vfill)
+                    __attribute__((always_inline)) {
+    issue_k(t + 3, kfill);
+    issue_v(t + 2, vfill);
+    __builtin_amdgcn_sched_barrier(0);
+    qk(kn);
+    pv(vc);
+    // Keep every operand read six MFMAs ahead of its use across the 32 MFMAs
+    // of the phase (16 K operands of one read, then 16 V operands of two):
+    // the default schedule reads each operand just before its MFMA, which
+    // leaves a lone wave waiting on LDS latency.  Six K reads first, then
+    // MFMA i followed by the reads of operand i + 6.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    // keys past S (the ragged last tile, or the tile after the last, whose
+    // scores come from reloaded data and must weigh nothing)
+    if ((t + 1) * kBc + kBc > S) mask_tail(t + 1);
+    __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+    __builtin_amdgcn_sched_barrier(0);
+    barrier();
+  };
+
+  // ---- prologue: K(0..2), V(0..1) in flight; S(0) ----
   issue_k(0, lds_k0);
   issue_v(0, lds_v0);
-  if (nkt > 1) issue_k(1, lds_k1);
-  wait_loads_and_sync();
-  f32x16 s_cur[2];
-  qk(lds_k0, s_cur);
-  if (tail && nkt == 1) mask_tail(0, s_cur);
-  update_max(s_cur);
-  // every wave has read lds_k0 before anyone refills it
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+  issue_k(1, lds_k1);
+  issue_v(1, lds_v1);
+  issue_k(2, lds_k2);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  barrier();
+  qk(lds_k0);
+  if (kBc > S) mask_tail(0);
+  if (!group_a) barrier();  // group B starts one phase later
 
-  // One pipelined step for tile j (which has a successor): tile j+1's K is in
-  // k_next, tile j's V in v_cur; V(j+1) goes to v_fill and K(j+2) to k_fill.
-  // s_in holds S(j); S(j+1) is written to s_out (the two register sets swap
-  // roles from one step to the next, so nothing is copied).
-  auto step = [&](int j, const char* k_next, const char* v_cur, char* v_fill, char* k_fill,
-                  f32x16* s_in, f32x16* s_out) {
-    issue_v(j + 1, v_fill);
-    if (j + 2 < nkt) issue_k(j + 2, k_fill);
-    uint32_t pk[2][8];
-    softmax_p(s_in, pk);
-    qk(k_next, s_out);
-    pv(v_cur, pk);
-    if (tail && j + 2 == nkt) mask_tail(j + 1, s_out);
-    update_max(s_out);
-    wait_loads_and_sync();
-  };
-
-  // ---- main loop, unrolled by two so every LDS buffer and score register
-  // set is named statically ----
-  f32x16 s_alt[2];
-  int j = 0;
-  for (; j + 2 < nkt; j += 2) {
-    step(j, lds_k1, lds_v0, lds_v1, lds_k0, s_cur, s_alt);
-    step(j + 1, lds_k0, lds_v1, lds_v0, lds_k1, s_alt, s_cur);
+  // three tiles per iteration, so every ring buffer is named statically
+  int t = 0;
+  for (; t + 3 <= nkt; t += 3) {
+    phase1();
+    phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
+    phase1();
+    phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+    phase1();
+    phase2(t + 2, lds_k0, lds_v2, lds_k2, lds_v1);
   }
-  bool in_alt = false;
-  if (j + 1 < nkt) {
-    step(j, lds_k1, lds_v0, lds_v1, lds_k0, s_cur, s_alt);
-    in_alt = true;
-    ++j;
+  if (t < nkt) {
+    phase1();
+    phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
   }
-
-  // ---- last tile (j = nkt - 1); every register set is named statically ----
-  auto last_tile = [&](const f32x16* s_last) {
-    uint32_t pk[2][8];
-    softmax_p(s_last, pk);
-    if (j & 1)
-      pv(lds_v1, pk);
-    else
-      pv(lds_v0, pk);
-  };
-  if (in_alt)
-    last_tile(s_alt);
-  else
-    last_tile(s_cur);
+  if (t + 1 < nkt) {
+    phase1();
+    phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+  }
+  if (group_a) barrier();  // matches group B's extra one
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
   const float inv = 1.0f / sum_halves((l4[0] + l4[1]) + (l4[2] + l4[3]));
   if (qrow < S) {
