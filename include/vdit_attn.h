@@ -77,7 +77,14 @@ vdit_status vdit_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * for vdit_attn_fwd_fp8.  Follows V-Smooth (VC-Attention article, section 02:
  * subtract a mean, quantise only the residual per channel in E4M3) and the
  * Q/K smoothing of section 01.  With nb = ceil(S / 64):
- *   q8, k8, v8  : [B,H,S,D] uint8 E4M3 codes (out).
+ *   q8, k8      : [B,H,S,D] uint8 E4M3 codes (out).
+ *   v8          : [B,H,nb,D,64] uint8 E4M3 codes (out), the layout the fp8
+ *                 attention kernel loads tile by tile: per 64-token block a
+ *                 tile of D channel rows x 64 key slots; slot s of a row holds
+ *                 key 32((s>>4)&1) + 8((s>>2)&3) + 4(s>>5) + (s&3) of the block,
+ *                 the four 16-byte chunks of channel row d are XOR-swizzled by
+ *                 (d >> 2) & 3, and keys past S hold code 0.  Note the size:
+ *                 B*H*nb*64*D bytes, which exceeds B*H*S*D when S % 64 != 0.
  *   q_scale     : [B,H,nb] float, amax/448 of each 64-token Q block (out).
  *   k_mean      : [B,H,k_mean_blocks,D] float (out); k_mean_blocks = nb gives
  *                 one mean per 64-token block (valid tokens only), = 1 one
@@ -108,15 +115,16 @@ vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v,
 size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean_blocks);
 
 /*
- * fp8 attention forward on the pre-pass outputs (same shapes as above).
+ * fp8 attention forward on the pre-pass outputs (same shapes and layouts as
+ * above, v8 tiled).
  * Scores: s_ij = q_scale_b(i) k_scale_b(j) (q8_i . k8_j) + q_hat_i . k_mean_b(j)
  * (the second term restores the K mean; it is kept even when k_mean_blocks = 1
  * makes it constant along a row, because it moves the grid P is rounded on).
- * Softmax in the log2 domain with
- * an integer running reference; P is quantised as E4M3(448 * p) for the fp8
- * P.V product while the row sum uses the fp32 p; the epilogue adds v_mean
- * back (VC-Attention article, section 02, Restore):
- *   o = v_scale * (sum_j P8_ij v8_j) / (448 l_i) + v_mean, bf16 out.
+ * Softmax in the log2 domain with an integer running reference; P is
+ * quantised as P8 = E4M3(448 * p) for the fp8 P.V product and the row sum is
+ * that of the quantised weights, so the weights of a row sum to one and the
+ * mean restore is exact (VC-Attention article, section 02, Restore):
+ *   o = v_scale * (sum_j P8_ij v8_j) / (sum_j P8_ij) + v_mean, bf16 out.
  * Float arrays must be 16-byte aligned.
  */
 vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,

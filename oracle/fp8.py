@@ -193,8 +193,11 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
     Steps: dequantise Q_hat = dec(q8) q_scale, K_hat = dec(k8) k_scale,
     V_hat = dec(v8) v_scale;  s_ij = scale (Q_hat_i . K_hat_j + Q_hat_i .
     k_mean_b(j));  t = log2(e) s;  M_i = ceil(max_j t_ij);  p = 2^(t - M);
-    l_i = sum_j p_ij;  w = dec(E4M3(p_scale p)) / p_scale (or w = p without
-    P quantisation);  O_i = (sum_j w_ij V_hat_j) / l_i + v_mean.
+    w = dec(E4M3(p_scale p)) / p_scale (or w = p without P quantisation);
+    l_i = sum_j w_ij;  O_i = (sum_j w_ij V_hat_j) / l_i + v_mean.
+    The row sum is that of the weights actually applied to V, so each row's
+    weights sum to one and the mean restore of the VC-Attention article
+    (section 02, Restore: sum_j P_j v_mean / l = v_mean) holds exactly.
     """
     S, D = qz["q8"].shape
     nb = qz["q_scale"].shape[0]
@@ -213,8 +216,8 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
         t = (qh[rr] @ keff.T) * (float(np.float64(scale)) * log2e)
         M = np.ceil(t.max(axis=1, keepdims=True))
         p = np.exp2(t - M)
-        l = p.sum(axis=1, keepdims=True)
         w = e4m3_decode(e4m3_encode(p * p_scale)) / p_scale if p_quant else p
+        l = w.sum(axis=1, keepdims=True)
         out[r0:r0 + chunk] = (w @ vh) / l + qz["v_mean"].astype(np.float64)[None, :]
     return out
 

@@ -59,3 +59,36 @@ def sample_rows(S, n_random=96, tile=128, seed=0):
 
 def workload_heads(H):
     return sorted({0, H // 2, H - 1})
+
+
+# The fp8 pre-pass writes V codes as the attention kernel reads them: per
+# 64-token block a [128 channel][64 slot] tile; slot s holds key
+# 32((s>>4)&1) + 8((s>>2)&3) + 4(s>>5) + (s&3) of the block, and the four
+# 16-byte chunks of channel row d are XOR-swizzled by (d >> 2) & 3.
+def _v8_tile_keys():
+    d = np.arange(128)[:, None]
+    pos = np.arange(64)[None, :]
+    sl = 16 * ((pos >> 4) ^ ((d >> 2) & 3)) + (pos & 15)
+    return 32 * ((sl >> 4) & 1) + 8 * ((sl >> 2) & 3) + 4 * (sl >> 5) + (sl & 3)  # [128, 64]
+
+
+def tile_v8(codes):
+    """[B, H, S, 128] codes -> [B, H, ceil(S/64), 128, 64] kernel layout."""
+    codes = np.asarray(codes)
+    B, H, S, D = codes.shape
+    nb = -(-S // 64)
+    pad = np.zeros((B, H, nb * 64, D), codes.dtype)
+    pad[:, :, :S] = codes
+    keys = _v8_tile_keys()
+    blk = pad.reshape(B, H, nb, 64, D)
+    return blk[:, :, :, keys, np.arange(D)[:, None]]
+
+
+def untile_v8(tiled, S):
+    """Inverse of tile_v8: [B, H, nb, 128, 64] -> [B, H, S, 128]."""
+    tiled = np.asarray(tiled)
+    B, H, nb, D, _ = tiled.shape
+    keys = _v8_tile_keys()
+    out = np.zeros((B, H, nb, 64, D), tiled.dtype)
+    out[:, :, :, keys, np.arange(D)[:, None]] = tiled
+    return out.reshape(B, H, nb * 64, D)[:, :, :S]

@@ -20,7 +20,7 @@ from oracle import fp8 as ofp8
 from video_diffusion_transformer_vdit_amd import binding, inputs
 
 from gpu_util import (FP8_COS, FP8_MAX_ABS, FP8_MODEL_MEAN_REL, f32_of, log, round_bf16,
-                      sample_rows, to_dev, to_dev_any, workload_heads)
+                      sample_rows, tile_v8, to_dev, to_dev_any, untile_v8, workload_heads)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +36,13 @@ def gpu_quant(q, k, v, k_mean_blocks=None):
 
 
 def compare_quant(zg, zo, heads=None, what=""):
+    """Bit-exact comparison; the GPU's V codes are read back from the
+    kernel's tiled layout first."""
+    S = zo["q8"].shape[2]
     for key in KEYS:
         g = zg[key].cpu().numpy()
+        if key == "v8":
+            g = untile_v8(g, S)
         o = zo[key]
         if heads is not None:
             g = g[:, heads]
@@ -113,7 +118,8 @@ def quantize_threaded(q, k, v, threads=8):
 
 
 def zdev(zo):
-    return {key: to_dev_any(zo[key]) for key in KEYS}
+    """The oracle's pre-pass outputs on the GPU, V codes in the kernel's tiled layout."""
+    return {key: to_dev_any(tile_v8(zo[key]) if key == "v8" else zo[key]) for key in KEYS}
 
 
 @pytest.mark.parametrize("mode", ["block", "global"])

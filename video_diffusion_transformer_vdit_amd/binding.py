@@ -121,7 +121,9 @@ def quant_buffers(B, H, S, k_mean_blocks=None, device="cuda"):
     return {
         "q8": torch.empty((B, H, S, HEAD_DIM), **u8),
         "k8": torch.empty((B, H, S, HEAD_DIM), **u8),
-        "v8": torch.empty((B, H, S, HEAD_DIM), **u8),
+        # V codes in the attention kernel's layout: per 64-token block a
+        # [128 channel][64 key slot] tile (see include/vdit_attn.h)
+        "v8": torch.empty((B, H, nb, HEAD_DIM, FP8_BLOCK), **u8),
         "q_scale": torch.empty((B, H, nb), **f32),
         "k_scale": torch.empty((B, H, nb), **f32),
         "k_mean": torch.empty((B, H, kmb, HEAD_DIM), **f32),

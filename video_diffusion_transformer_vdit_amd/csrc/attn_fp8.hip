@@ -18,30 +18,32 @@
 // does not change the softmax but it does move the fp8 grid P is rounded on.
 // Softmax runs in the log2 domain with an integer running reference m
 // (the ceiling of the running row maximum): p = 2^(t - m) <= 1.  P is
-// quantised as E4M3(448 p) for the fp8 PV product; the row sum takes the fp32
-// 448 p; because m only moves by whole powers of two, the quantised weights
-// equal those taken against the final row maximum (outside the subnormal
-// range).  Epilogue: o = v_scale (sum_j P8_ij v8_j) / l_i + v_mean.
+// quantised as P8 = E4M3(448 p) for the fp8 PV product; because m only moves
+// by whole powers of two, the quantised weights equal those taken against
+// the final row maximum (outside the subnormal range).  The row sum is that
+// of the quantised weights, formed by one more fp8 MFMA per tile against an
+// all-ones operand, so the weights of a row sum to exactly one and the mean
+// restore is exact.  Epilogue: o = v_scale (sum_j P8_ij v8_j) / (sum_j P8_ij)
+// + v_mean.
 //
-// Layout of the work: one workgroup = 4 waves x 32 queries; K/V tiles of 64
-// keys (= one scale block) staged through registers into a double-buffered
-// LDS ring; scores are produced transposed (S^T = K Q^T) so each lane owns
-// one query; V is transposed at staging time so that the P^T operand is the
-// S^T accumulator registers in order.
+// Work layout (the bf16 kernel's): one workgroup = 8 waves x 32 queries, one
+// workgroup per CU; scores transposed (S^T = K Q^T) so each lane owns one
+// query; K tiles (row-major, 16-byte chunks XOR-swizzled by key & 7) and V
+// tiles (already transposed and permuted by the pre-pass) go global -> LDS by
+// DMA into three-deep rings; waves 0-3 and 4-7 run the exponential phase and
+// the MFMA phase of each tile one phase apart (ping-pong).
 #include "device_common.h"
 #include "launchers.h"
 
 namespace vdit {
 namespace {
 
-constexpr int kBr = 128;
-constexpr int kBc = 64;
-constexpr int kThreads = 256;
-constexpr int kKStride = kHeadDim + 16;  // bytes per K8 row in LDS (144)
-constexpr int kVStride = kBc + 16;       // bytes per V8^T row in LDS (80)
-constexpr int kKBuf = kBc * kKStride;
-constexpr int kVBuf = kHeadDim * kVStride;
-constexpr int kCompBlocks = 32;          // K-mean blocks per compensation batch
+constexpr int kWaves = 8;
+constexpr int kBr = 32 * kWaves;  // 256 queries per workgroup
+constexpr int kBc = 64;           // keys per tile = one scale block
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileBytes = kBc * kHeadDim;  // 8 KB of codes
+constexpr int kCompBlocks = 32;             // K-mean blocks per compensation batch
 constexpr float kLog2P8 = 8.807354922057604f;  // log2(448)
 
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -54,64 +56,8 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p, bool ok) {
   return ok ? *reinterpret_cast<const u32x4*>(p) : z;
 }
 
-__device__ __forceinline__ u32x2 ld8(const uint8_t* p, bool ok) {
-  u32x2 z = {0u, 0u};
-  return ok ? *reinterpret_cast<const u32x2*>(p) : z;
-}
-
-struct Staged {
-  u32x4 k[2];  // K8 row t/4, bytes 32*(t%4) .. +31
-  u32x2 v[4];  // V8 rows 4*(t/16) .. +3, bytes 8*(t%16) .. +7
-  float ks;    // k_scale of the tile
-};
-
-__device__ __forceinline__ void load_tile(Staged& st, const uint8_t* K8h, const uint8_t* V8h,
-                                          const float* ksh, int j, int S, int tid) {
-  const int key0 = j * kBc;
-  const int kr = key0 + (tid >> 2);
-  const int kc = (tid & 3) * 32;
-  st.k[0] = ld16(K8h + (size_t)kr * kHeadDim + kc, kr < S);
-  st.k[1] = ld16(K8h + (size_t)kr * kHeadDim + kc + 16, kr < S);
-  const int vc = (tid & 15) * 8;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int vr = key0 + 4 * (tid >> 4) + i;
-    st.v[i] = ld8(V8h + (size_t)vr * kHeadDim + vc, vr < S);
-  }
-  st.ks = ksh[j];
-}
-
-// Byte e of lane half h in the PV operand is key 32(e/16) + 8((e%16)/4) + 4h + e%4
-// of the tile; V8^T keeps keys in that order: key bits [5|4:3|2|1:0] = a,b,h,r
-// go to position bits [5|4|3:2|1:0] = h,a,b,r.
-__device__ __forceinline__ int vpos(int key) {
-  return ((key >> 2) & 1) << 5 | ((key >> 5) & 1) << 4 | ((key >> 3) & 3) << 2 | (key & 3);
-}
-
-__device__ __forceinline__ void store_tile(const Staged& st, uint8_t* Ks, uint8_t* Vs, int tid) {
-  uint8_t* kd = Ks + (tid >> 2) * kKStride + (tid & 3) * 32;
-  *reinterpret_cast<u32x4*>(kd) = st.k[0];
-  *reinterpret_cast<u32x4*>(kd + 16) = st.k[1];
-  const int g = tid >> 4, c = tid & 15;
-  const int pos = vpos(4 * g);
-  // 4 keys x 8 channels -> 8 dwords of 4 keys each
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const uint32_t a0 = st.v[0][w], a1 = st.v[1][w], a2 = st.v[2][w], a3 = st.v[3][w];
-    const uint32_t lo01 = __byte_perm(a0, a1, 0x5140);  // a0.b0 a1.b0 a0.b1 a1.b1
-    const uint32_t hi01 = __byte_perm(a0, a1, 0x7362);  // a0.b2 a1.b2 a0.b3 a1.b3
-    const uint32_t lo23 = __byte_perm(a2, a3, 0x5140);
-    const uint32_t hi23 = __byte_perm(a2, a3, 0x7362);
-    const uint32_t d0 = __byte_perm(lo01, lo23, 0x5410);  // channel 4w+0: keys 0..3
-    const uint32_t d1 = __byte_perm(lo01, lo23, 0x7632);  // channel 4w+1
-    const uint32_t d2 = __byte_perm(hi01, hi23, 0x5410);  // channel 4w+2
-    const uint32_t d3 = __byte_perm(hi01, hi23, 0x7632);  // channel 4w+3
-    const int ch = 8 * c + 4 * w;
-    *reinterpret_cast<uint32_t*>(Vs + (ch + 0) * kVStride + pos) = d0;
-    *reinterpret_cast<uint32_t*>(Vs + (ch + 1) * kVStride + pos) = d1;
-    *reinterpret_cast<uint32_t*>(Vs + (ch + 2) * kVStride + pos) = d2;
-    *reinterpret_cast<uint32_t*>(Vs + (ch + 3) * kVStride + pos) = d3;
-  }
+__device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
 // E4M3 code (from the OCP format: bias 7, 3 mantissa bits, subnormals 2^-9)
@@ -125,56 +71,97 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 
 // kBlockMean: one K mean per 64-token block (else one mean per head)
 template <bool kBlockMean>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const float* __restrict__ k_mean, const float* __restrict__ v_mean,
     const float* __restrict__ v_scale, uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2 * kKBuf];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * kVBuf];
-  __shared__ float lds_comp[4][kCompBlocks][32];
+  // three-deep rings of K and V tiles, one LDS object per buffer
+  __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v2[kTileBytes];
+  __shared__ float lds_comp[kWaves][kCompBlocks][32];
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
   const int qt = tile - bh * n_qtiles;
   const size_t base = (size_t)bh * S * kHeadDim;
-  const int nb = (S + kBc - 1) / kBc;
+  const int nkt = (S + kBc - 1) / kBc;
   const uint8_t* Q8h = Q8 + base;
-  const uint8_t* K8h = K8 + base;
-  const uint8_t* V8h = V8 + base;
-  const float* ksh = k_scale + (size_t)bh * nb;
+  const char* K8h = reinterpret_cast<const char*>(K8 + base);
+  // V codes: nkt tiles of 8 KB per head
+  const char* V8h = reinterpret_cast<const char*>(V8) + (size_t)bh * nkt * kTileBytes;
+  const float* ksh = k_scale + (size_t)bh * nkt;
   uint16_t* Oh = O + base;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qt * kBr + wave * 32 + col;
   const bool qok = qrow < S;
+  const bool tail = (S % kBc) != 0;
 
+  // ---- DMA: one 1 KB load per wave per tile and tensor ----
+  // K: wave w fills tile rows 8w .. 8w+7; lane i writes physical chunk i%8 of
+  // row 8w + i/8 and fetches the logical chunk the swizzle maps there.
+  const int krow = 8 * wave + (lane >> 3);
+  const int kgo = krow * kHeadDim + 16 * ((lane & 7) ^ (krow & 7));
+  const uint32_t wslice = (uint32_t)wave * 1024;
+  auto issue_k = [&](int t, const void* buf) __attribute__((always_inline)) {
+    t = min(t, nkt - 1);  // past the end: reload the last tile into a free buffer
+    const int key0 = t * kBc;
+    const char* src = K8h + (size_t)key0 * kHeadDim;
+    int go = kgo;
+    if (tail && t == nkt - 1) go = (min(key0 + krow, S - 1) - key0) * kHeadDim + 16 * ((lane & 7) ^ (krow & 7));
+    dma16(src, (uint32_t)go, lds_addr(buf) + wslice);
+  };
+  auto issue_v = [&](int t, const void* buf) __attribute__((always_inline)) {
+    t = min(t, nkt - 1);
+    dma16(V8h + (size_t)t * kTileBytes, (uint32_t)(wslice + 16 * lane), lds_addr(buf) + wslice);
+  };
+  // K operand of key block kb, channel step kk: lane (key 32kb + col, half)
+  // reads logical chunks 4kk + 2half + {0, 1} of its key row.
+  int koff[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) koff[kk][h2] = col * kHeadDim + 16 * ((4 * kk + 2 * half + h2) ^ (col & 7));
+  // V^T operand of channel block mb: lane (channel 32mb + col, half) reads
+  // key slots 32half .. +31 = logical chunks 2half + {0, 1} of its row.
+  int voff[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) voff[h2] = col * kBc + 16 * ((2 * half + h2) ^ ((col >> 2) & 3));
+
+  // ---- Q operand (registers for the whole loop) ----
   i32x8 qf[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const uint8_t* p = Q8h + (size_t)qrow * kHeadDim + 64 * kk + 32 * half;
-    const u32x4 lo = ld16(p, qok), hi = ld16(p + 16, qok);
-    qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    qf[kk] = join(ld16(p, qok), ld16(p + 16, qok));
   }
   // all 32 queries of a wave sit in one 64-token scale block
-  const float qsc = q_scale[(size_t)bh * nb + min(qrow, S - 1) / kBc] * c;
+  const float qsc = q_scale[(size_t)bh * nkt + min(qrow, S - 1) / kBc] * c;
 
   // dec(q8) in bf16 (exact) as the B operand of the K-mean MFMAs (lane:
   // query col, channels 16kk + 8half .. +7).
   bf16x8 qh[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    const u32x2 w = ld8(Q8h + (size_t)qrow * kHeadDim + 16 * kk + 8 * half, qok);
+    const uint8_t* p = Q8h + (size_t)qrow * kHeadDim + 16 * kk + 8 * half;
+    const u32x2 w = qok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) qh[kk][e] = (__bf16)e4m3_value((w[e >> 2] >> (8 * (e & 3))) & 255u);
   }
-  const int nbm = kBlockMean ? nb : 1;
+  const int nbm = kBlockMean ? nkt : 1;
   const float* kmh = k_mean + (size_t)bh * nbm * kHeadDim;
   // dec(q8_i) . k_mean_b for b = b0 .. b0+31 (clamped to the last block),
-  // written to this wave's LDS slots lds_comp[wave][b - b0][query].
-  auto kmean_batch = [&](int b0) {
+  // written to this wave's LDS slots lds_comp[wave][b - b0][query].  Each
+  // wave reads only its own slots, after its own writes (LDS operations of
+  // one wave complete in order), so no barrier is needed around them.
+  auto kmean_batch = [&](int b0) __attribute__((always_inline)) {
     f32x16 cm;
 #pragma unroll
     for (int i = 0; i < 16; ++i) cm[i] = 0.f;
@@ -196,115 +183,184 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) lds_comp[wave][8 * (i >> 2) + 4 * half + (i & 3)][col] = cm[i];
   };
-  // Each wave reads only its own slots, after its own writes (LDS operations
-  // of one wave complete in order), so no barrier is needed around them.
   float cb_global = 0.f;
   if (!kBlockMean) {
     kmean_batch(0);
     cb_global = lds_comp[wave][0][col] * qsc;
   }
 
-  f32x16 acc[4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
-  float m_ref = -INFINITY;
-  float l = 0.f;
-
-  const int nkt = nb;
-  Staged st;
-  load_tile(st, K8h, V8h, ksh, 0, S, tid);
-  store_tile(st, lds_k, lds_v, tid);
-  float ks_cur = st.ks;
-  __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (kBlockMean && (j % kCompBlocks) == 0) kmean_batch(j);
-    if (j + 1 < nkt) load_tile(st, K8h, V8h, ksh, j + 1, S, tid);
-    const uint8_t* Ks = lds_k + buf * kKBuf;
-    const uint8_t* Vs = lds_v + buf * kVBuf;
-
-    f32x16 s[2];
+  f32x16 s[2];  // S^T of one tile: key block kb, lane (q, half): keys 32kb + 8(i/4) + 4half + i%4
+  auto qk = [&](const char* Kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint8_t* p = Ks + (32 * kb + col) * kKStride + 64 * kk + 32 * half;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
-        const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const char* p = Kb + kb * 32 * kHeadDim;
+        const i32x8 a = join(*reinterpret_cast<const u32x4*>(p + koff[kk][0]),
+                             *reinterpret_cast<const u32x4*>(p + koff[kk][1]));
         s[kb] = mfma32x32x64_fp8(a, qf[kk], s[kb]);
       }
     }
-    if (j == nkt - 1 && (S % kBc) != 0) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j * kBc + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (key >= S) s[kb][i] = -INFINITY;
-        }
-    }
-    // t = a * dot + cb (log2 domain); a >= 0, so the row max of t is at the
-    // row max of dot.
-    const float a = qsc * ks_cur;
-    const float cb = kBlockMean ? lds_comp[wave][j % kCompBlocks][col] * qsc : cb_global;
-    float mx = s[0][0];
+  };
+  auto mask_tail = [&](int t) __attribute__((always_inline)) {
+    // keeps the compiler from turning this once-per-workgroup branch into
+    // selects executed on every tile
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    float mnew = fmaf(mx, a, cb);
-    mnew = fmaxf(mnew, swap_halves(mnew));
+      for (int i = 0; i < 16; ++i) {
+        const int key = t * kBc + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (key >= S) s[kb][i] = -INFINITY;
+      }
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+  // row sum of the quantised weights: every row of ones x P^T is the column sum
+  f32x16 lacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
+  float m_ref = -INFINITY;
+
+  // P8 of tile t: t = a dot + cb in the log2 domain (a >= 0, so the row max
+  // of t is at the row max of dot); reference update and (rare) rescale;
+  // e = 2^(t - m) * 448 <= 448 up to the last bit of exp2, packed as E4M3.
+  uint32_t pk[8];
+  auto softmax_p = [&](int t) __attribute__((always_inline)) {
+    const float a = qsc * ksh[t];
+    const float cb = kBlockMean ? lds_comp[wave][t % kCompBlocks][col] * qsc : cb_global;
+    float t8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      t8[u] = fmaxf(fmaxf(s[u >> 2][4 * (u & 3)], s[u >> 2][4 * (u & 3) + 1]),
+                    fmaxf(s[u >> 2][4 * (u & 3) + 2], s[u >> 2][4 * (u & 3) + 3]));
+    const float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
+                           fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
+    const float mnew = fmaf(mx, a, cb);
     if (__ballot(mnew > m_ref) != 0ull) {
-      const float mnext = mnew > m_ref ? ceilf(mnew) : m_ref;
+      // rare: keep it a real branch rather than 80 multiplies per tile
+      asm volatile("" ::: "memory");
+      const float mq = max_halves(mnew);
+      const float mnext = mq > m_ref ? ceilf(mq) : m_ref;
       const float alpha = exp2_fast(m_ref - mnext);
-      l *= alpha;
+      lacc *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
+      for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
       m_ref = mnext;
     }
     const float bias = cb + kLog2P8 - m_ref;
-    uint32_t pk[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        float e[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          e[u] = fminf(exp2_fast(fmaf(s[kb][4 * p + u], a, bias)), 448.0f);
-          l += e[u];
-        }
-        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
-        pk[4 * kb + p] = w;
+        const float e0 = exp2_fast(fmaf(s[kb][4 * p], a, bias));
+        const float e1 = exp2_fast(fmaf(s[kb][4 * p + 1], a, bias));
+        const float e2 = exp2_fast(fmaf(s[kb][4 * p + 2], a, bias));
+        const float e3 = exp2_fast(fmaf(s[kb][4 * p + 3], a, bias));
+        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        pk[4 * kb + p] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
       }
+  };
+  // O^T += V^T P^T (one 32x32x64 MFMA per 32-channel block) and the row sum
+  auto pv = [&](const char* Vb) __attribute__((always_inline)) {
     const i32x8 pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3],
                       (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const uint8_t* p = Vs + (32 * mb + col) * kVStride + 32 * half;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
-      const i32x8 av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const char* p = Vb + mb * 32 * kBc;
+      const i32x8 av = join(*reinterpret_cast<const u32x4*>(p + voff[0]),
+                            *reinterpret_cast<const u32x4*>(p + voff[1]));
       acc[mb] = mfma32x32x64_fp8(av, pb, acc[mb]);
     }
+    lacc = mfma32x32x64_fp8(ones, pb, lacc);
+  };
 
-    if (j + 1 < nkt) {
-      store_tile(st, lds_k + (buf ^ 1) * kKBuf, lds_v + (buf ^ 1) * kVBuf, tid);
-      ks_cur = st.ks;
-    }
-    __syncthreads();
+  // workgroup barrier that the compiler moves no memory access across
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // ---- two wave groups in ping-pong (as in the bf16 kernel) ----
+  // Phase P1(t): P8 of tile t (VALU); phase P2(t): S of tile t+1 and
+  // O += P8(t) V(t) (MFMA), plus the K-mean batch for the next 32 tiles when
+  // tile t+1 starts one.  Waves 4-7 run one phase behind waves 0-3; a barrier
+  // ends every phase.  At the start of P2(t) every wave issues its share of
+  // K(t+3) and V(t+2), into the buffers of K(t) and V(t-1), which both groups
+  // have finished reading by then; every wave waits for all but its newest
+  // two loads before each barrier.
+  const bool group_a = wave < 4;
+  auto phase1 = [&](int t) __attribute__((always_inline)) {
+    softmax_p(t);
+    // consume P here: otherwise the exponentials are moved to their use
+    // after the barrier, into the MFMA phase
+    asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]), "v"(pk[4]), "v"(pk[5]),
+                 "v"(pk[6]), "v"(pk[7]));
+    __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2): all but the newest batch
+    __builtin_amdgcn_sched_barrier(0);
+    barrier();
+  };
+  auto phase2 = [&](int t, const char* kn, const char* vc, const void* kfill, const void* vfill)
+                    __attribute__((always_inline)) {
+    issue_k(t + 3, kfill);
+    issue_v(t + 2, vfill);
+    __builtin_amdgcn_sched_barrier(0);
+    qk(kn);
+    pv(vc);
+    // keys past S (the ragged last tile, or the tile after the last, whose
+    // scores come from reloaded data and must weigh nothing)
+    if ((t + 1) * kBc + kBc > S) mask_tail(t + 1);
+    if (kBlockMean && ((t + 1) % kCompBlocks) == 0 && t + 1 < nkt) kmean_batch(t + 1);
+    __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
+    __builtin_amdgcn_sched_barrier(0);
+    barrier();
+  };
+
+  // ---- prologue: K(0..2), V(0..1) in flight; S(0) ----
+  issue_k(0, lds_k0);
+  issue_v(0, lds_v0);
+  issue_k(1, lds_k1);
+  issue_v(1, lds_v1);
+  issue_k(2, lds_k2);
+  if (kBlockMean) kmean_batch(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  barrier();
+  qk(lds_k0);
+  if (kBc > S) mask_tail(0);
+  if (!group_a) barrier();  // group B starts one phase later
+
+  // three tiles per iteration, so every ring buffer is named statically
+  int t = 0;
+  for (; t + 3 <= nkt; t += 3) {
+    phase1(t);
+    phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
+    phase1(t + 1);
+    phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+    phase1(t + 2);
+    phase2(t + 2, lds_k0, lds_v2, lds_k2, lds_v1);
   }
+  if (t < nkt) {
+    phase1(t);
+    phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
+  }
+  if (t + 1 < nkt) {
+    phase1(t + 1);
+    phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+  }
+  if (group_a) barrier();  // matches group B's extra one
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  const float inv = 1.0f / (l + swap_halves(l));
+  const float inv = 1.0f / lacc[0];
   if (qok) {
     const float* vsh = v_scale + (size_t)bh * kHeadDim;
     const float* vmh = v_mean + (size_t)bh * kHeadDim;

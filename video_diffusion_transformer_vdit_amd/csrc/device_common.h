@@ -54,4 +54,49 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ lds_void* lds_ptr(void* p) { return (lds_void*)p; }
+
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// global_load_lds_dwordx4 written out: 16 bytes per lane from gbase + voff
+// to LDS address m0 + 16 * lane.  Issued through asm so that the compiler
+// does not track the LDS write (it cannot tell the K/V buffers apart and
+// would wait for every DMA before each LDS read); the kernel waits for these
+// loads itself (s_waitcnt vmcnt + s_barrier) before any wave reads the
+// buffer.  M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(uniform_ptr(gbase))
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
+}
+
+// max / sum of the values held by lanes l and l ^ 32
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace vdit

@@ -15,6 +15,13 @@
 //      1/scale (workspace), k_mean (global mode)
 //   3. per (b,h, block): V residual codes; K residual codes (global mode)
 //
+// V codes are written as the attention kernel reads them: per (b,h) and
+// 64-token block one 8 KB tile of 128 channel rows x 64 key slots, slot s of
+// a row holding key 32((s>>4)&1) + 8((s>>2)&3) + 4(s>>5) + (s&3) of the block
+// (the order of the P^T operand of the 32x32x64 fp8 MFMA), with the four
+// 16-byte chunks of a row XOR-swizzled by (channel >> 2) & 3 so that the
+// kernel's LDS reads are free of bank conflicts.  Keys past S are code 0.
+//
 // Integer-valued decisions are taken in a stated precision so they can be
 // checked bit for bit: sums of bf16 values in fp64 (exact for these inputs),
 // mean = fp32(sum / n), residual = fp32(x - mean), scale = fp32(amax / 448)
@@ -296,6 +303,7 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
     uint8_t* __restrict__ V8, float* __restrict__ k_scale, const float* __restrict__ k_mean,
     const float* __restrict__ v_mean, Workspace ws, int S, int nb, int k_global) {
   __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock][kHeadDim];  // [key][channel]
   const int bh = blockIdx.x / nb;
   const int blk = blockIdx.x - bh * nb;
   const int tid = threadIdx.x;
@@ -312,6 +320,7 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = rg + 16 * p;
+    u32x2 w = {0u, 0u};
     if (r < nvalid) {
       const size_t off = head + (size_t)(row0 + r) * kHeadDim + 8 * c;
       float f[8];
@@ -319,10 +328,33 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
       uint32_t cd[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) cd[i] = e4m3_rne(clamp448(__fmul_rn(__fsub_rn(f[i], vm[i]), vi[i])));
-      u32x2 w;
       w.x = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
       w.y = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
-      *reinterpret_cast<u32x2*>(V8 + off) = w;
+    }
+    *reinterpret_cast<u32x2*>(&tile[r][8 * c]) = w;
+  }
+  __syncthreads();
+  // transpose into the kernel's tile: thread -> (channel d, physical chunk pc)
+  {
+    uint8_t* V8t = V8 + ((size_t)bh * nb + blk) * (kBlock * kHeadDim);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int idx = tid + kThreads * h;  // 0 .. 511
+      const int d = idx >> 2, pc = idx & 3;
+      const int lc = pc ^ ((d >> 2) & 3);
+      uint32_t wd[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int sl = 16 * lc + 4 * q + b;  // key slot
+          const int key = 32 * ((sl >> 4) & 1) + 8 * ((sl >> 2) & 3) + 4 * (sl >> 5) + (sl & 3);
+          acc |= (uint32_t)tile[key][d] << (8 * b);
+        }
+        wd[q] = acc;
+      }
+      *reinterpret_cast<u32x4*>(V8t + d * kBlock + 16 * pc) = u32x4{wd[0], wd[1], wd[2], wd[3]};
     }
   }
   if (k_global) {
