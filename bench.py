@@ -209,6 +209,8 @@ def main():
         o8 = torch.empty_like(q)
         ms_q = time_launches(lambda: binding.vdit_attn_quant_fp8(q, k, v, out=z), args.steps, args.warmup)
         ms_a = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o8), args.steps, args.warmup)
+        ms_x = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o8, expcast=True),
+                             args.steps, args.warmup)
         prepass_bytes = w.B * w.H * w.S * w.D * (2 * 3 + 2 + 1 + 2 + 1)  # reads Q,K,V,V(again); writes 3 codes
         result["fp8"] = {
             "attention_ms": round(ms_a, 4),
@@ -217,6 +219,9 @@ def main():
             "prepass_ms": round(ms_q, 4),
             "prepass_gbs": round(prepass_bytes / (ms_q * 1e-3) / 1e9, 1),
             "combined_tflops": round(w.flop / ((ms_a + ms_q) * 1e-3) / 1e12, 2),
+            "expcast_attention_ms": round(ms_x, 4),
+            "expcast_attention_tflops": round(w.flop / (ms_x * 1e-3) / 1e12, 2),
+            "expcast_attention_peak_fraction": round(w.flop / (ms_x * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
         }
         del z, o8
     del o

@@ -134,6 +134,24 @@ vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                               void* o, int B, int H, int S, int D, float scale,
                               void* stream);
 
+/*
+ * ExpCast-FP8 variant of vdit_attn_fwd_fp8 (VC-Attention article, section 03):
+ * same arguments and result definition, except that the P8 byte is written
+ * directly from the log domain instead of exp2 followed by an E4M3
+ * conversion.  The E4M3 byte of v read as an integer is about 8 log2(v) + 56;
+ * with the article's centring constant -0.35 and P scaled by 448:
+ *   P8_ij = rne(8 (t_ij - m_i) + 8 log2(448) + 55.65), clamped to [0, 255]
+ * (t <= m keeps it <= 126, the code of 448; bytes below 8 decode as E4M3
+ * subnormals).  One FMA and one convert per weight; it agrees with the exact
+ * byte in about 79.6% of weights and is otherwise one code away.
+ */
+vdit_status vdit_attn_fwd_fp8_expcast(const void* q8, const void* k8, const void* v8,
+                                      const float* q_scale, const float* k_scale,
+                                      const float* k_mean, int k_mean_blocks,
+                                      const float* v_mean, const float* v_scale,
+                                      void* o, int B, int H, int S, int D, float scale,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,8 +12,12 @@ Sources on the pages
 * V-Smooth: subtract a mean, quantise only the residual per channel in
   E4M3, add the mean back using the online-softmax row sum, no second pass
   [VC-Attention article, §02, Demean and Restore].
-* The E4M3 byte read as an integer is close to 8*log2(v) + 56 [VC-Attention
-  article, §03].
+* The E4M3 byte read as an integer is close to 8*log2(v) + 56; ExpCast-FP8
+  writes the byte of a softmax weight from its log-domain score with one
+  multiply-add and the centring constant -0.35; it matches the exp-then-cast
+  byte in 79.6% of cases per doubling and is otherwise one code off; the
+  per-row total variation stays under 3.64% plus underflow tails
+  [VC-Attention article, §03].
 
 Readings taken where the pages are silent (each also listed in the design
 notes): Q and K use one scale per 64-token block; K is smoothed by the mean
@@ -21,8 +25,10 @@ of each 64-token block (or one global mean per head), and the per-block mean
 is compensated exactly by adding q_hat . k_mean_b to the scores of block b;
 V is smoothed by one per-channel mean over the sequence with one per-channel
 scale; P is quantised as E4M3(448 * 2^(t - M)) where t is the log2-domain
-score and M the integer ceiling of the row maximum of t; the row sum uses
-the unquantised P.
+score and M the integer ceiling of the row maximum of t; the row sum is the
+sum of the quantised weights (so the weights of a row sum to one and the
+mean restore is exact); ExpCast rounds 8 (t - M) + 8 log2(448) + 55.65 to
+the nearest integer, ties to even, clamped to [0, 255].
 
 Precision of the integer-valued decisions (codes): the pre-pass takes them
 in the precision the kernel takes them in, so the codes can be compared bit
@@ -185,16 +191,46 @@ def quantize(q, k, v, block: int = 64, k_mean: str = "block"):
             for key in parts[0][0]}
 
 
+# ExpCast-FP8 (VC-Attention article, section 03): the E4M3 byte of a value
+# v, read as an integer, is about 8 log2(v) + 56; the article writes the byte
+# of a weight directly from its log-domain score with one multiply-add and a
+# centring constant beta = -0.35.  Here the weight is 448 p with log2 p =
+# t - M, so the byte is round-to-nearest-even of 8 (t - M) + 8 log2(448) + 56
+# - 0.35, clamped to the byte range (t <= M keeps it <= 126, the code of 448).
+EXPCAST_BETA = -0.35
+EXPCAST_OFFSET = 8.0 * math.log2(E4M3_MAX) + 56.0 + EXPCAST_BETA
+
+
+def expcast_byte(log2_v) -> np.ndarray:
+    """ExpCast byte of a value given by its base-2 logarithm (no P scale)."""
+    x = 8.0 * np.asarray(log2_v, np.float64) + 56.0 + EXPCAST_BETA
+    return np.clip(np.rint(x), 0, 255).astype(np.uint8)
+
+
 def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
                              p_quant: bool = True, p_scale: float = E4M3_MAX,
-                             chunk: int = 256) -> np.ndarray:
+                             chunk: int = 256, p_cast: str = "exp",
+                             reference: str | None = None) -> np.ndarray:
     """Quantisation model of the fp8 attention for one head, in fp64.
 
     Steps: dequantise Q_hat = dec(q8) q_scale, K_hat = dec(k8) k_scale,
     V_hat = dec(v8) v_scale;  s_ij = scale (Q_hat_i . K_hat_j + Q_hat_i .
     k_mean_b(j));  t = log2(e) s;  M_i = ceil(max_j t_ij);  p = 2^(t - M);
-    w = dec(E4M3(p_scale p)) / p_scale (or w = p without P quantisation);
+    w = dec(E4M3(p_scale p)) / p_scale (or w = p without P quantisation;
+    with p_cast="expcast" the E4M3 byte is the ExpCast byte of p_scale p,
+    expcast_byte(t - M + log2(p_scale)));
     l_i = sum_j w_ij;  O_i = (sum_j w_ij V_hat_j) / l_i + v_mean.
+
+    ``reference`` says which M the weights are taken against: "final" (the
+    row maximum, above) or "running", the online softmax's reference: keys
+    are taken in order in tiles of ``block``; before a tile's weights are
+    written the reference rises to ceil(max t) of the tile if that is larger,
+    and the sums so far are scaled by 2^(M_old - M_new).  For the exp-then-
+    cast path the two agree except for weights in E4M3's subnormal range;
+    the ExpCast byte map is not scale-invariant below byte 8 (the subnormal
+    codes), so for ExpCast the weights depend on the reference they were
+    written against, and the running one (default for ExpCast) is the online
+    method's.
     The row sum is that of the weights actually applied to V, so each row's
     weights sum to one and the mean restore of the VC-Attention article
     (section 02, Restore: sum_j P_j v_mean / l = v_mean) holds exactly.
@@ -211,12 +247,36 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.empty((rows.size, D), np.float64)
     log2e = 1.0 / math.log(2.0)
+    if reference is None:
+        reference = "running" if p_cast == "expcast" else "final"
+
+    def weights(t, M):
+        if p_cast == "expcast":
+            return e4m3_decode(expcast_byte(t - M + math.log2(p_scale))) / p_scale
+        p = np.exp2(t - M)
+        return e4m3_decode(e4m3_encode(p * p_scale)) / p_scale if p_quant else p
+
     for r0 in range(0, rows.size, chunk):
         rr = rows[r0:r0 + chunk]
         t = (qh[rr] @ keff.T) * (float(np.float64(scale)) * log2e)
+        if reference == "running":
+            M = np.full((rr.size, 1), -np.inf)
+            acc = np.zeros((rr.size, D))
+            l = np.zeros((rr.size, 1))
+            for j0 in range(0, S, block):
+                tt = t[:, j0:j0 + block]
+                Mn = np.maximum(M, np.ceil(tt.max(axis=1, keepdims=True)))
+                f = np.where(np.isfinite(M), np.exp2(M - Mn), 0.0)
+                acc *= f
+                l *= f
+                M = Mn
+                w = weights(tt, M)
+                acc += w @ vh[j0:j0 + block]
+                l += w.sum(axis=1, keepdims=True)
+            out[r0:r0 + chunk] = acc / l + qz["v_mean"].astype(np.float64)[None, :]
+            continue
         M = np.ceil(t.max(axis=1, keepdims=True))
-        p = np.exp2(t - M)
-        w = e4m3_decode(e4m3_encode(p * p_scale)) / p_scale if p_quant else p
+        w = weights(t, M)
         l = w.sum(axis=1, keepdims=True)
         out[r0:r0 + chunk] = (w @ vh) / l + qz["v_mean"].astype(np.float64)[None, :]
     return out

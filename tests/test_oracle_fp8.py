@@ -294,3 +294,132 @@ def test_metrics():
     assert fp8.cosine(a, 2 * a) == pytest.approx(1.0)
     assert fp8.max_abs(a, a + [0, 0.5, 0]) == 0.5
     assert fp8.mean_rel_l1(a + [0.6, 0, 0], a) == pytest.approx(0.1)
+
+
+# ---- ExpCast-FP8 (VC-Attention article, section 03) ----
+
+def test_expcast_byte_is_log_affine_at_powers_of_two():
+    """The E4M3 byte of 2^k, read as an integer, is exactly 8k + 56 (the
+    format: exponent field k + 7, zero mantissa) over the normal range."""
+    for k in range(-6, 9):
+        assert int(fp8.e4m3_encode(np.array([2.0 ** k]))[0]) == 8 * k + 56
+
+
+def test_expcast_matches_exact_cast_796_percent_per_octave():
+    """The article's figures: per doubling of the value, the direct byte
+    equals the exp-then-cast byte in 79.6% of cases and otherwise differs by
+    one code."""
+    u = (np.arange(200000) + 0.5) / 200000
+    for k in (-5, -1, 0, 3, 7):
+        v = 2.0 ** (u + k)
+        exact = fp8.e4m3_encode(v).astype(np.int64)
+        cast = fp8.expcast_byte(u + k).astype(np.int64)
+        d = cast - exact
+        assert abs(float(np.mean(d == 0)) - 0.796) < 0.0015, k
+        assert int(np.max(np.abs(d))) == 1
+
+
+def test_expcast_total_variation_bound():
+    """The article's per-row bound: the ratio r of the ExpCast value to 2^t
+    stays in [a, b] with (sqrt b - sqrt a)/(sqrt b + sqrt a) = 3.64%, the
+    largest total variation such a ratio can cause between normalised
+    weights; rows of scores without underflow stay under it."""
+    table = fp8.e4m3_table()
+    u = (np.arange(100000) + 0.5) / 100000 + 2
+    r = table[fp8.expcast_byte(u)] / 2.0 ** u
+    a, b = r.min(), r.max()
+    bound = (math.sqrt(b) - math.sqrt(a)) / (math.sqrt(b) + math.sqrt(a))
+    assert abs(bound - 0.0364) < 0.0005
+    g = np.random.default_rng(12)
+    for sd in (0.5, 1.0, 2.0):
+        t = g.standard_normal(4096) * sd
+        m = math.ceil(t.max())
+        p = 2.0 ** (t - m)
+        w = table[fp8.expcast_byte(t - m + math.log2(448))] / 448
+        tv = 0.5 * np.abs(w / w.sum() - p / p.sum()).sum()
+        assert tv < bound
+
+
+def test_expcast_model_uses_the_direct_bytes():
+    """Model with p_cast='expcast' = the textbook weighted mean with the
+    ExpCast weights, written out for a tiny head."""
+    S, D = 12, 128
+    z = _random_qz(S, D, 22, 1)
+    scale = 0.09
+    got = fp8.attention_fp8_model_head(z, scale, p_cast="expcast")
+    table = fp8.e4m3_table()
+    qh = fp8.e4m3_decode(z["q8"]) * float(z["q_scale"][0])
+    kh = fp8.e4m3_decode(z["k8"]) * float(z["k_scale"][0]) + z["k_mean"][0].astype(np.float64)
+    vh = fp8.e4m3_decode(z["v8"]) * z["v_scale"].astype(np.float64)
+    t = (qh @ kh.T) * scale / math.log(2.0)
+    for i in range(S):
+        m = math.ceil(t[i].max())
+        x = 8 * (t[i] - m) + 8 * math.log2(448) + 56 - 0.35
+        w = np.array([table[int(min(max(np.rint(xx), 0), 255))] for xx in x])
+        o = (w @ vh) / w.sum() + z["v_mean"]
+        np.testing.assert_allclose(got[i], o, rtol=1e-12, atol=1e-12)
+
+
+def test_expcast_running_reference_bruteforce():
+    """Online reference (tiles of 64 keys in order): plain loops over tiles
+    and keys; the reference rises only at tiles whose maximum exceeds it, the
+    sums so far are scaled by the power of two, and each tile's bytes are
+    written against the reference then in force."""
+    S, D = 150, 128
+    z = _random_qz(S, D, 23, 1)
+    # keys past the first tile copy their queries, so a row's own key (a
+    # large score q.q) arrives after the first tile
+    z["k8"][64:] = z["q8"][64:]
+    scale = 0.15
+    got = fp8.attention_fp8_model_head(z, scale, p_cast="expcast", rows=np.arange(0, S, 17))
+    table = fp8.e4m3_table()
+    dec = lambda c: float(table[int(c)])
+    log2e = 1.0 / math.log(2.0)
+    kh = [[dec(z["k8"][j, d]) * float(z["k_scale"][j // 64]) + float(z["k_mean"][0, d]) for d in range(D)]
+          for j in range(S)]
+    rose = 0
+    for n, i in enumerate(range(0, S, 17)):
+        qi = [dec(z["q8"][i, d]) * float(z["q_scale"][i // 64]) for d in range(D)]
+        t = [sum(a * b for a, b in zip(qi, kh[j])) * scale * log2e for j in range(S)]
+        m = None
+        acc = [0.0] * D
+        l = 0.0
+        for j0 in range(0, S, 64):
+            mt = math.ceil(max(t[j0:j0 + 64]))
+            if m is None or mt > m:
+                f = 0.0 if m is None else 2.0 ** (m - mt)
+                rose += m is not None
+                acc = [x * f for x in acc]
+                l *= f
+                m = mt
+            for j in range(j0, min(j0 + 64, S)):
+                x = 8 * (t[j] - m) + 8 * math.log2(448) + 56 - 0.35
+                b = int(min(max(round_half_even(x), 0), 255))
+                wj = dec(b) / 448
+                l += wj
+                for d in range(D):
+                    acc[d] += wj * dec(z["v8"][j, d]) * float(z["v_scale"][d])
+        for d in range(0, D, 31):
+            o = acc[d] / l + float(z["v_mean"][d])
+            assert abs(got[n, d] - o) <= 1e-12 * (1 + abs(o))
+    assert rose > 0  # the case exercises a rising reference
+
+
+def round_half_even(x):
+    r = math.floor(x + 0.5)
+    if r - x == 0.5 and r % 2 == 1:
+        r -= 1
+    return r
+
+
+def test_expcast_running_equals_final_when_the_maximum_comes_first():
+    """If every row's maximum lies in the first tile the reference never
+    moves, and the online weights are those against the row maximum."""
+    S, D = 256, 128
+    z = _random_qz(S, D, 24, 1)
+    z["k8"][64:] = (z["k8"][64:] & 0x80) | np.minimum(z["k8"][64:] & 0x7F, 0x20)  # small late keys
+    z["k8"][:64] = (z["k8"][:64] & 0x80) | np.maximum(z["k8"][:64] & 0x7F, 0x50)
+    scale = 0.05
+    run = fp8.attention_fp8_model_head(z, scale, p_cast="expcast", reference="running")
+    fin = fp8.attention_fp8_model_head(z, scale, p_cast="expcast", reference="final")
+    np.testing.assert_allclose(run, fin, rtol=1e-12, atol=1e-12)

@@ -181,3 +181,47 @@ def test_end_to_end_within_quantisation_floor(name):
             f"ideal-quantisation floor cos={fl_cos:.6f} max_abs={fl_ma:.3e}")
         assert 1 - cos <= 1.5 * (1 - fl_cos) + 1e-5
         assert ma <= 1.5 * fl_ma + 1e-3
+
+
+# ---- ExpCast-FP8 entry point (P bytes written from the log domain) ----
+
+@pytest.mark.parametrize("mode", ["block", "global"])
+@pytest.mark.parametrize("S,seed", [(1, 31), (63, 32), (200, 33), (1000, 34)])
+def test_expcast_vs_quant_model_sweep(S, seed, mode):
+    import torch
+    B, H = 1, 2
+    q, k, v = rand_bits((B, H, S, 128), seed), rand_bits((B, H, S, 128), seed + 10, 1.0, 0.5), \
+        rand_bits((B, H, S, 128), seed + 20, 1.0, 1.0)
+    zo = ofp8.quantize(q, k, v, k_mean=mode)
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE, expcast=True)
+    torch.cuda.synchronize()
+    got = f32_of(o)
+    ref = ofp8.attention_fp8_model(zo, SCALE, p_cast="expcast")
+    check_model(got, ref, f"expcast S={S} {mode}")
+
+
+def test_expcast_workload_vs_model_and_truth():
+    """Full-size launch: against the ExpCast quantisation model on sampled
+    rows of three heads, and end to end (GPU pre-pass) against the truth
+    within the floor the ExpCast model itself reaches."""
+    import torch
+    w = inputs.get_workload("wan2.1-14b-720p-fp8")
+    q, k, v = inputs.make_inputs(w)
+    z = gpu_quant(q, k, v)
+    o = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.S, n_random=32)
+    heads = workload_heads(w.H)[:2]
+    got = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+    del o, z
+    for i, h in enumerate(heads):
+        zh = ofp8.quantize_head(q[0, h], k[0, h], v[0, h])
+        model = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows, p_cast="expcast")
+        check_model(got[i], model, f"expcast workload head {h}")
+        truth = oa.attention_head(q[0, h], k[0, h], v[0, h], SCALE, rows=rows)
+        fl_cos, fl_ma = ofp8.cosine(model, truth), ofp8.max_abs(model, truth)
+        cos, ma = ofp8.cosine(got[i], truth), ofp8.max_abs(got[i], truth)
+        log(f"expcast head {h} vs truth: gpu cos={cos:.6f} max_abs={ma:.3e} | "
+            f"ExpCast-model floor cos={fl_cos:.6f} max_abs={fl_ma:.3e}")
+        assert 1 - cos <= 1.5 * (1 - fl_cos) + 1e-5
+        assert ma <= 1.5 * fl_ma + 1e-3

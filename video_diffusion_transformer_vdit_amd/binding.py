@@ -30,6 +30,7 @@ SIGNATURES = {
                                  _I, _I, _I, _I, _P]),
     "vdit_attn_quant_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "vdit_attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
+    "vdit_attn_fwd_fp8_expcast": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
 }
 
 _lib = None
@@ -153,9 +154,10 @@ def vdit_attn_quant_fp8(q, k, v, k_mean_blocks=None, out=None, stream=None):
     return z
 
 
-def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None):
+def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False):
     """fp8 attention on pre-pass outputs ``z`` (dict as from vdit_attn_quant_fp8);
-    returns bf16 o [B, H, S, 128]."""
+    returns bf16 o [B, H, S, 128].  ``expcast`` selects the ExpCast-FP8 entry
+    point (P bytes written directly from the log domain)."""
     import torch
     B, H, S, D = _shape4(z["q8"])
     if o is None:
@@ -163,7 +165,8 @@ def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None):
     scale = D ** -0.5 if scale is None else float(scale)
     kmb = int(z["k_mean"].shape[2])
     lib = load()
-    check(lib.vdit_attn_fwd_fp8(
+    fn = lib.vdit_attn_fwd_fp8_expcast if expcast else lib.vdit_attn_fwd_fp8
+    check(fn(
         _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),
         _dev(z["v8"], torch.uint8, "v8"), _dev(z["q_scale"], torch.float32, "q_scale"),
         _dev(z["k_scale"], torch.float32, "k_scale"), _dev(z["k_mean"], torch.float32, "k_mean"),

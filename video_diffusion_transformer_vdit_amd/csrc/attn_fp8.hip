@@ -45,6 +45,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTileBytes = kBc * kHeadDim;  // 8 KB of codes
 constexpr int kCompBlocks = 32;             // K-mean blocks per compensation batch
 constexpr float kLog2P8 = 8.807354922057604f;  // log2(448)
+// ExpCast-FP8: the E4M3 byte of a value v, read as an integer, is about
+// 8 log2(v) + 56 (VC-Attention article, section 03); with the article's
+// centring constant -0.35 and P scaled by 448, the byte of 448 p with
+// log2 p = t - m is rne(8 (t - m) + 8 log2(448) + 55.65).
+constexpr float kExpCastOffset = 8.0f * 8.807354922057604f + 56.0f - 0.35f;
 
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // operand formats 0/0 = E4M3 x E4M3; no block scales
@@ -69,8 +74,10 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
-// kBlockMean: one K mean per 64-token block (else one mean per head)
-template <bool kBlockMean>
+// kBlockMean: one K mean per 64-token block (else one mean per head);
+// kExpCast: P8 bytes written directly from the log domain (else exp2, then
+// an E4M3 conversion)
+template <bool kBlockMean, bool kExpCast>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
@@ -256,18 +263,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
       m_ref = mnext;
     }
-    const float bias = cb + kLog2P8 - m_ref;
+    if (kExpCast) {
+      // byte = rne(8 (t - m) + offset), one FMA and one saturating convert
+      // (v_cvt_pk_u8_f32: round to nearest even, clamp to [0, 255]); t <= m
+      // keeps it <= 126, the code of 448
+      const float a8 = 8.0f * a, b8 = 8.0f * (cb - m_ref) + kExpCastOffset;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float e0 = exp2_fast(fmaf(s[kb][4 * p], a, bias));
-        const float e1 = exp2_fast(fmaf(s[kb][4 * p + 1], a, bias));
-        const float e2 = exp2_fast(fmaf(s[kb][4 * p + 2], a, bias));
-        const float e3 = exp2_fast(fmaf(s[kb][4 * p + 3], a, bias));
-        uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-        pk[4 * kb + p] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
-      }
+        for (int p = 0; p < 4; ++p) {
+          uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p], a8, b8), 0, 0u);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 1], a8, b8), 1, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 2], a8, b8), 2, w);
+          pk[4 * kb + p] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 3], a8, b8), 3, w);
+        }
+    } else {
+      const float bias = cb + kLog2P8 - m_ref;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float e0 = exp2_fast(fmaf(s[kb][4 * p], a, bias));
+          const float e1 = exp2_fast(fmaf(s[kb][4 * p + 1], a, bias));
+          const float e2 = exp2_fast(fmaf(s[kb][4 * p + 2], a, bias));
+          const float e3 = exp2_fast(fmaf(s[kb][4 * p + 3], a, bias));
+          uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+          pk[4 * kb + p] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+        }
+    }
   };
   // O^T += V^T P^T (one 32x32x64 MFMA per 32-channel block) and the row sum
   auto pv = [&](const char* Vb) __attribute__((always_inline)) {
@@ -381,12 +404,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   }
 }
 
+template <bool kExpCast>
+void launch_fp8(bool block_mean, unsigned blocks, hipStream_t stream, const uint8_t* q,
+                const uint8_t* k, const uint8_t* v, const float* q_scale, const float* k_scale,
+                const float* k_mean, const float* v_mean, const float* v_scale, uint16_t* out,
+                int S, int n_qtiles, float c) {
+  if (block_mean)
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, kExpCast>), dim3(blocks), dim3(kThreads), 0, stream,
+                       q, k, v, q_scale, k_scale, k_mean, v_mean, v_scale, out, S, n_qtiles, c);
+  else
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, kExpCast>), dim3(blocks), dim3(kThreads), 0,
+                       stream, q, k, v, q_scale, k_scale, k_mean, v_mean, v_scale, out, S, n_qtiles,
+                       c);
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                const float* q_scale, const float* k_scale, const float* k_mean,
                                int k_mean_blocks, const float* v_mean, const float* v_scale,
-                               void* o, int B, int H, int S, float scale, hipStream_t stream) {
+                               void* o, int B, int H, int S, float scale, bool expcast,
+                               hipStream_t stream) {
   const int n_qtiles = (S + kBr - 1) / kBr;
   const unsigned blocks = (unsigned)((long long)B * H * n_qtiles);
   const int nb = (S + kBc - 1) / kBc;
@@ -396,12 +434,12 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
   const uint8_t* v = static_cast<const uint8_t*>(v8);
   uint16_t* out = static_cast<uint16_t*>(o);
   const float c = scale * kLog2e;
-  if (block_mean)
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, q, k, v,
-                       q_scale, k_scale, k_mean, v_mean, v_scale, out, S, n_qtiles, c);
+  if (expcast)
+    launch_fp8<true>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean, v_scale,
+                     out, S, n_qtiles, c);
   else
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, q, k,
-                       v, q_scale, k_scale, k_mean, v_mean, v_scale, out, S, n_qtiles, c);
+    launch_fp8<false>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean, v_scale,
+                      out, S, n_qtiles, c);
   return hipGetLastError();
 }
 

@@ -130,10 +130,10 @@ size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean
   return vdit::quant_fp8_workspace_bytes(B, H, S, k_mean_blocks);
 }
 
-vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
-                              const float* q_scale, const float* k_scale, const float* k_mean,
-                              int k_mean_blocks, const float* v_mean, const float* v_scale,
-                              void* o, int B, int H, int S, int D, float scale, void* stream) {
+static vdit_status fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
+                           const float* k_scale, const float* k_mean, int k_mean_blocks,
+                           const float* v_mean, const float* v_scale, void* o, int B, int H, int S,
+                           int D, float scale, bool expcast, void* stream) {
   VDIT_TRY(check_ptr(q8, "q8"));
   VDIT_TRY(check_ptr(k8, "k8"));
   VDIT_TRY(check_ptr(v8, "v8"));
@@ -149,8 +149,25 @@ vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
   if (k_mean_blocks != 1 && k_mean_blocks != nb)
     return fail(VDIT_ERR_UNSUPPORTED, "%s", "k_mean_blocks must be 1 or ceil(S/64)");
   return hip_result(vdit::launch_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks,
-                                              v_mean, v_scale, o, B, H, S, scale,
+                                              v_mean, v_scale, o, B, H, S, scale, expcast,
                                               static_cast<hipStream_t>(stream)));
+}
+
+vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                              const float* q_scale, const float* k_scale, const float* k_mean,
+                              int k_mean_blocks, const float* v_mean, const float* v_scale,
+                              void* o, int B, int H, int S, int D, float scale, void* stream) {
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, v_scale, o, B, H, S,
+                 D, scale, false, stream);
+}
+
+vdit_status vdit_attn_fwd_fp8_expcast(const void* q8, const void* k8, const void* v8,
+                                      const float* q_scale, const float* k_scale,
+                                      const float* k_mean, int k_mean_blocks, const float* v_mean,
+                                      const float* v_scale, void* o, int B, int H, int S, int D,
+                                      float scale, void* stream) {
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, v_scale, o, B, H, S,
+                 D, scale, true, stream);
 }
 
 }  // extern "C"

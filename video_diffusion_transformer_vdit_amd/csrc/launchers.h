@@ -20,6 +20,7 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                const float* q_scale, const float* k_scale,
                                const float* k_mean, int k_mean_blocks,
                                const float* v_mean, const float* v_scale, void* o,
-                               int B, int H, int S, float scale, hipStream_t stream);
+                               int B, int H, int S, float scale, bool expcast,
+                               hipStream_t stream);
 
 }  // namespace vdit
