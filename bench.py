@@ -192,7 +192,7 @@ def main():
         "peak_fraction": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_kernel",
+            "kernel": "attn_fwd_bf16_kernel<false>",
             "achieved": round(tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -201,6 +201,23 @@ def main():
             "algorithmic_flop_per_launch": w.flop,
             "algorithmic_bytes_per_launch": 4 * w.B * w.H * w.S * w.D * 2,
         },
+    }
+
+    # block-causal variant, one chunk per latent frame; FLOP counts only the
+    # scored (query, key) pairs: sum over rows of the row's key limit
+    chunk = w.tokens_per_frame
+    rows = np.arange(w.S, dtype=np.int64)
+    pairs = int(np.minimum((rows // chunk + 1) * chunk, w.S).sum())
+    causal_flop = 4 * w.B * w.H * pairs * w.D
+    log("[bench] bf16 block-causal attention")
+    ms_c = time_launches(lambda: binding.vdit_attn_fwd_block_causal(q, k, v, chunk, o=o, scale=scale),
+                         args.steps, args.warmup)
+    result["block_causal"] = {
+        "chunk": chunk,
+        "scored_pair_fraction": round(pairs / (w.S * w.S), 4),
+        "ms": round(ms_c, 4),
+        "tflops": round(causal_flop / (ms_c * 1e-3) / 1e12, 2),
+        "peak_fraction": round(causal_flop / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
     }
 
     if not args.no_fp8:

@@ -73,6 +73,22 @@ vdit_status vdit_attn_fwd(const void* q, const void* k, const void* v, void* o,
                           void* stream);
 
 /*
+ * Block-causal variant of vdit_attn_fwd for chunk-wise (frame-block) video
+ * generation: query i attends to key j iff floor(j / chunk) <= floor(i / chunk),
+ * i.e. every token sees its own chunk and all earlier ones (the Wave Forcing
+ * note on airadar.tv: later blocks read the context of earlier blocks; a
+ * chunk is a group of latent frames, e.g. 3600 tokens per 720p latent frame).
+ *   o[b,h,i,:] = sum_{j < lim(i)} softmax_j(scale * q_i . k_j) v_j,
+ *   lim(i) = min(S, (floor(i / chunk) + 1) * chunk).
+ * Key tiles past a workgroup's largest limit are not visited.  chunk >= S is
+ * full attention.  Arguments, layouts and errors as vdit_attn_fwd, plus
+ * VDIT_ERR_INVALID_ARG for chunk < 1.
+ */
+vdit_status vdit_attn_fwd_block_causal(const void* q, const void* k, const void* v, void* o,
+                                       int B, int H, int S, int D, float scale, int chunk,
+                                       int dtype, void* stream);
+
+/*
  * fp8 pre-pass: quantise and smooth bf16 Q, K, V to E4M3 (OCP E4M3FN, max 448)
  * for vdit_attn_fwd_fp8.  Follows V-Smooth (VC-Attention article, section 02:
  * subtract a mean, quantise only the residual per channel in E4M3) and the

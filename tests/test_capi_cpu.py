@@ -118,3 +118,17 @@ def _load_fresh(path):
         return binding.load(path)
     finally:
         binding._lib = saved
+
+
+def test_block_causal_and_expcast_validation():
+    lib = binding.load()
+    st = lib.vdit_attn_fwd_block_causal(A, A * 2, A * 3, A * 4, 1, 1, 16, 128, 0.1, 0, 0, None)
+    assert st == 1 and b"chunk" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_block_causal(A, A * 2, A * 3, A * 4, 1, 1, 16, 64, 0.1, 4, 0, None)
+    assert st == 2 and b"D = 128" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_block_causal(None, A * 2, A * 3, A * 4, 1, 1, 16, 128, 0.1, 4, 0, None)
+    assert st == 1 and b"null pointer: q" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_expcast(A, A, A, A, A, A, 4, A, A, A, 1, 2, 200, 128, 0.0, None)
+    assert st == 1 and b"scale" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_expcast(A, A, A, A, A, A, 5, A, A, A, 1, 2, 200, 128, 0.1, None)
+    assert st == 2 and b"k_mean_blocks" in lib.vdit_last_error()

@@ -148,3 +148,55 @@ def test_full_size_workload_sampled(name):
         log(f"{name}: oracle head {h} ({rows.size} rows)")
         ref = oa.attention_head(q[0, h], k[0, h], v[0, h], SCALE, rows=rows)
         check_close(got_all[i], ref, f"{name} head {h}")
+
+
+# ---- block-causal variant (query i sees key j iff j // chunk <= i // chunk) ----
+
+def run_causal(q_bits, k_bits, v_bits, chunk, scale=SCALE):
+    import torch
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    o = binding.vdit_attn_fwd_block_causal(q, k, v, chunk, scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("S,chunk", [(1, 1), (65, 1), (65, 64), (300, 17), (300, 100), (1000, 256),
+                                     (1000, 513), (2049, 700), (777, 5000)])
+def test_block_causal_sweep(S, chunk):
+    g = np.random.default_rng(S + chunk)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((1, 2, S, 128)).astype(np.float32)) for _ in range(3)]
+    log(f"block-causal S={S} chunk={chunk}")
+    got = f32_of(run_causal(*x, chunk))
+    ref = oa.attention(*x, SCALE, allowed=oa.block_causal_allowed(S, chunk))
+    check_close(got, ref, f"block-causal S={S} chunk={chunk}", ulp_slack=True)
+
+
+def test_block_causal_with_chunk_past_s_is_full_attention_bitwise():
+    import torch
+    g = np.random.default_rng(41)
+    x = [to_dev(inputs.f32_to_bf16_bits(g.standard_normal((2, 3, 1500, 128)).astype(np.float32)))
+         for _ in range(3)]
+    a = binding.vdit_attn_fwd(*x, scale=SCALE)
+    b = binding.vdit_attn_fwd_block_causal(*x, 1500, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_block_causal_full_size_sampled():
+    """720p workload with one chunk per latent frame (3,600 tokens), oracle
+    rows sampled on three heads, including rows at chunk boundaries."""
+    import torch
+    w = inputs.get_workload("wan2.1-14b-720p")
+    chunk = 3600
+    q, k, v = inputs.make_inputs(w)
+    o = run_causal(q, k, v, chunk)
+    rows = np.unique(np.concatenate([sample_rows(w.S, n_random=48),
+                                     np.array([0, 1, 3599, 3600, 3601, 36000, 71999, 72000])]))
+    heads = workload_heads(w.H)
+    got_all = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+    del o
+    torch.cuda.empty_cache()
+    for i, h in enumerate(heads):
+        ref = oa.attention_head(q[0, h], k[0, h], v[0, h], SCALE, rows=rows,
+                                allowed=oa.block_causal_allowed(w.S, chunk))
+        check_close(got_all[i], ref, f"block-causal 720p head {h}")

@@ -26,6 +26,7 @@ SIGNATURES = {
     "vdit_status_str": (ctypes.c_char_p, [_I]),
     "vdit_last_error": (ctypes.c_char_p, []),
     "vdit_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
+    "vdit_attn_fwd_block_causal": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "vdit_attn_quant_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _Z,
                                  _I, _I, _I, _I, _P]),
     "vdit_attn_quant_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
@@ -105,6 +106,23 @@ def vdit_attn_fwd(q, k, v, o=None, scale=None, stream=None):
     check(lib.vdit_attn_fwd(_dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
                             _dev(v, torch.bfloat16, "v"), _dev(o, torch.bfloat16, "o"),
                             B, H, S, D, scale, DTYPE_BF16, _stream(stream)))
+    return o
+
+
+def vdit_attn_fwd_block_causal(q, k, v, chunk, o=None, scale=None, stream=None):
+    """Block-causal attention by chunks of ``chunk`` tokens (query i sees key
+    j iff j // chunk <= i // chunk) for bf16 [B, H, S, 128]; returns o."""
+    import torch
+    B, H, S, D = _shape4(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if o is None:
+        o = torch.empty_like(q)
+    scale = D ** -0.5 if scale is None else float(scale)
+    lib = load()
+    check(lib.vdit_attn_fwd_block_causal(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(o, torch.bfloat16, "o"), B, H, S, D, scale, int(chunk), DTYPE_BF16, _stream(stream)))
     return o
 
 

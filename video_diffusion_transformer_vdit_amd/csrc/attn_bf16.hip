@@ -21,17 +21,25 @@
 //    Within a matrix phase every LDS operand read is issued six MFMAs ahead
 //    of its use.
 //  * K/V tiles go straight from global memory to LDS (global_load_lds_dwordx4,
-//    no register staging) into three-deep rings.  K is stored chunk-major
-//    ([16-byte chunk][key]), so the K operand of every MFMA is one 16-byte
-//    read at a linear offset and consecutive lanes read consecutive bytes.  V
-//    is stored row-major with its 16-byte chunks XOR-swizzled
-//    (chunk ^ 4*(row & 3)) and read with ds_read_b64_tr_b16, which hands each
-//    lane 4 keys of one channel; both reads are free of bank conflicts.
+//    no register staging) into three-deep rings.  Each load instruction
+//    covers four whole 256-byte rows, so global reads are fully coalesced.
+//    K is stored row-major with its 16-byte chunks XOR-swizzled by
+//    (row & 15): the 16 lanes that the LDS serves together read 16 different
+//    rows at 16 different bank groups.  V is stored row-major with its chunks
+//    XOR-swizzled by 4*(row & 3) and read with ds_read_b64_tr_b16, which
+//    hands each lane 4 keys of one channel; both reads are free of bank
+//    conflicts.  The swizzles are applied by choosing which global chunk each
+//    lane fetches, since the DMA writes 16 consecutive bytes per lane.
 //  * Online softmax in the log2 domain with an integer running reference
 //    m (ceil of the running maximum of scale*log2(e)*s): P = 2^(c s - m) <= 1,
 //    and the accumulator is rescaled (by an exact power of two) only in the
 //    rare tiles where some row's maximum exceeds its reference.  P is rounded
 //    to bf16 once; the row sum adds exactly those rounded weights.
+//  * Block-causal instance (chunk > 0): query i attends to key j iff
+//    j / chunk <= i / chunk, i.e. to keys below lim(i) = min(S, (i/chunk + 1)
+//    chunk).  A workgroup visits only the key tiles below the largest limit
+//    of its rows; keys at or past a row's limit score -inf.  Query tiles are
+//    dealt heaviest first.
 //  * Ragged tails: rows of the last K/V tile past S are read from row S-1
 //    (finite data), scored -inf, and so weigh exactly 0; queries >= S are
 //    computed on zeros and not stored.
@@ -59,9 +67,11 @@ __device__ __forceinline__ bf16x8 read_v_operand(const char* p0, const char* p1)
   return __builtin_bit_cast(bf16x8, v);
 }
 
+template <bool kBlockCausal>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, int S, int n_qtiles, float c,
+    int chunk) {
   // three-deep rings of K and V tiles, one LDS object per buffer
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
@@ -72,7 +82,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
-  const int qt = tile - bh * n_qtiles;
+  // heaviest query tiles first (they see the most keys when block-causal)
+  const int qt = n_qtiles - 1 - (tile - bh * n_qtiles);
   const size_t base = (size_t)bh * S * kHeadDim;
   const char* Kh = reinterpret_cast<const char*>(K + base);
   const char* Vh = reinterpret_cast<const char*>(V + base);
@@ -82,25 +93,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int qrow = qt * kBr + wave * 32 + col;
-  const int nkt = (S + kBc - 1) / kBc;
+  const int nkt_all = (S + kBc - 1) / kBc;
   const bool tail = (S % kBc) != 0;
+  // key limits: this lane's row, this wave's first (smallest) row, and the
+  // workgroup's last valid row (the largest)
+  auto key_limit = [&](int row) { return kBlockCausal ? min(S, (row / chunk + 1) * chunk) : S; };
+  const int lim = key_limit(min(qrow, S - 1));
+  const int wave_lim = key_limit(min(qt * kBr + wave * 32, S - 1));
+  const int nkt = (key_limit(min(qt * kBr + kBr - 1, S - 1)) + kBc - 1) / kBc;
 
   // ---- per-lane constant offsets ----
-  // V loads: wave w, load i covers tile rows 8w + 4i + lane/16; lane writes
-  // physical chunk lane%16 of its row, so it fetches the logical chunk that
-  // the swizzle maps there.  K loads: load i of wave w fills chunk row
-  // c = 2w + i (1 KB) with chunk c of all 64 keys (lane = key).
+  // K and V loads: wave w, load i covers tile rows 8w + 4i + lane/16; lane
+  // writes physical chunk lane%16 of its row, so it fetches the logical chunk
+  // that the row's swizzle maps there.
   const int lrow0 = 4 * kLoadsPerWave * wave + (lane >> 4);  // + 4i
   const int pchunk = lane & 15;
   int kgo[kLoadsPerWave], vgo[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
     const int r = lrow0 + 4 * i;
-    kgo[i] = lane * kRowBytes + 16 * (kLoadsPerWave * wave + i);
+    kgo[i] = r * kRowBytes + 16 * (pchunk ^ (r & 15));
     vgo[i] = r * kRowBytes + 16 * (pchunk ^ (4 * (r & 3)));
   }
-  // K operand: lane (key = 32kb + col, half) reads chunk 2kk + half of its key
-  const int kbase = half * 1024 + col * 16;
+  // K operand: lane (key = 32kb + col, half) reads chunk 2kk + half of its
+  // key, stored at physical chunk (2kk + half) ^ (key & 15)
+  int koff[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * kRowBytes + 16 * ((2 * kk + half) ^ (col & 15));
   // V operand: 16-lane group g = lane/16, s = lane%16 reads row
   // 16kc + 8r + 4(g>>1) + s/4, channels 32mb + 16(g&1) + 4(s%4) .. +3.
   const int g = lane >> 4, s16 = lane & 15;
@@ -117,11 +136,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const int key0 = t * kBc;
     const char* src = Kh + (size_t)key0 * kRowBytes;
     const uint32_t dst = lds_addr(buf) + wslice;
-    if (tail && t == nkt - 1) {
+    if (tail && t == nkt_all - 1) {
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int row = min(key0 + lane, S - 1);
-        const int go = (row - key0) * kRowBytes + 16 * (kLoadsPerWave * wave + i);
+        const int r = lrow0 + 4 * i;
+        const int row = min(key0 + r, S - 1);
+        const int go = (row - key0) * kRowBytes + 16 * (pchunk ^ (r & 15));
         dma16(src, (uint32_t)go, dst + i * 1024);
       }
     } else {
@@ -134,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const int key0 = t * kBc;
     const char* src = Vh + (size_t)key0 * kRowBytes;
     const uint32_t dst = lds_addr(buf) + wslice;
-    if (tail && t == nkt - 1) {
+    if (tail && t == nkt_all - 1) {
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int r = lrow0 + 4 * i;
@@ -170,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + 2048 * kk + 512 * kb + kbase);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + 32 * kRowBytes * kb + koff[kk]);
         s[kb] = mfma32x32x16_bf16(a, qf[kk], s[kb]);
       }
   };
@@ -183,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = t * kBc + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (key >= S) s[kb][i] = -INFINITY;
+        if (key >= lim) s[kb][i] = -INFINITY;
       }
   };
 
@@ -250,11 +270,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     }
   };
 
-  // workgroup barrier that the compiler moves no memory access across
+  // workgroup barrier that the compiler moves no instruction across (the
+  // exponentials of the next phase would otherwise be hoisted above it)
   auto barrier = [&]() __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- two wave groups in ping-pong ----
@@ -309,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     // keys past S (the ragged last tile, or the tile after the last, whose
     // scores come from reloaded data and must weigh nothing)
-    if ((t + 1) * kBc + kBc > S) mask_tail(t + 1);
+    if ((t + 1) * kBc + kBc > wave_lim) mask_tail(t + 1);
     __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
     __builtin_amdgcn_sched_barrier(0);
     barrier();
@@ -324,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   barrier();
   qk(lds_k0);
-  if (kBc > S) mask_tail(0);
+  if (kBc > wave_lim) mask_tail(0);
   if (!group_a) barrier();  // group B starts one phase later
 
   // three tiles per iteration, so every ring buffer is named statically
@@ -366,13 +388,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
-                                int B, int H, int S, float scale, hipStream_t stream) {
+                                int B, int H, int S, float scale, int chunk, hipStream_t stream) {
   const int n_qtiles = (S + kBr - 1) / kBr;
   const long long blocks = (long long)B * H * n_qtiles;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+  auto kernel = chunk > 0 ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), S, n_qtiles,
-                     scale * kLog2e);
+                     scale * kLog2e, chunk);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 namespace vdit {
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
-                                int B, int H, int S, float scale, hipStream_t stream);
+                                int B, int H, int S, float scale, int chunk, hipStream_t stream);
 
 size_t quant_fp8_workspace_bytes(int B, int H, int S, int k_mean_blocks);
 
