@@ -11,7 +11,9 @@ Sources on the pages
   §01].
 * V-Smooth: subtract a mean, quantise only the residual per channel in
   E4M3, add the mean back using the online-softmax row sum, no second pass
-  [VC-Attention article, §02, Demean and Restore].
+  [VC-Attention article, §02, Demean and Restore].  The article's own mean
+  is taken over each hardware block of 128 tokens and costs 0.125 bit per
+  value element, i.e. 16 bits per channel per block [same section].
 * The E4M3 byte read as an integer is close to 8*log2(v) + 56; ExpCast-FP8
   writes the byte of a softmax weight from its log-domain score with one
   multiply-add and the centring constant -0.35; it matches the exp-then-cast
@@ -24,7 +26,9 @@ notes): Q and K use one scale per 64-token block; K is smoothed by the mean
 of each 64-token block (or one global mean per head), and the per-block mean
 is compensated exactly by adding q_hat . k_mean_b to the scores of block b;
 V is smoothed by one per-channel mean over the sequence with one per-channel
-scale; P is quantised as E4M3(448 * 2^(t - M)) where t is the log2-domain
+scale, or (the article's Demean, ``v_mean="block"``) by the per-channel mean
+of each 128-token block (valid tokens only) rounded to bf16 (the 16-bit
+mean), with one per-channel scale of the residual over the sequence; P is quantised as E4M3(448 * 2^(t - M)) where t is the log2-domain
 score and M the integer ceiling of the row maximum of t; the row sum is the
 sum of the quantised weights (so the weights of a row sum to one and the
 mean restore is exact); ExpCast rounds 8 (t - M) + 8 log2(448) + 55.65 to
@@ -36,7 +40,9 @@ for bit:  means are fp64 sums of the bf16 inputs (exact here) divided in
 fp64 and rounded once to fp32;  residual = fp32(x - mean);  amax = max|r|;
 scale = fp32(amax / 448) and inv = fp32(448 / amax) (both from fp64
 quotients), or 1 and 0 when amax = 0;  code = E4M3_RNE(clamp(fp32(r * inv),
--448, 448)).
+-448, 448)).  The 16-bit block mean of V is bf16_rne(fp32 mean) and the
+residual is taken against that rounded mean, fp32(x - mean16), so that
+adding it back restores exactly what was subtracted.
 """
 
 from __future__ import annotations
@@ -130,6 +136,15 @@ def _codes(r32: np.ndarray, inv32) -> np.ndarray:
     return e4m3_encode(np.clip(prod, -E4M3_MAX, E4M3_MAX))
 
 
+def bf16_rne(x32) -> np.ndarray:
+    """Round float32 values to bfloat16, nearest even, returned as float32
+    (finite inputs): keep the top 16 bits of the fp32 pattern after adding
+    0x7FFF plus the lowest kept bit."""
+    u = np.asarray(x32, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
 def _mean32(x32: np.ndarray, axis: int) -> np.ndarray:
     """fp32(fp64 sum / n): the sum of bf16 values is exact in fp64 here."""
     n = x32.shape[axis]
@@ -137,14 +152,18 @@ def _mean32(x32: np.ndarray, axis: int) -> np.ndarray:
     return (s / float(n)).astype(np.float32)
 
 
-def quantize_head(q, k, v, block: int = 64, k_mean: str = "block"):
+def quantize_head(q, k, v, block: int = 64, k_mean: str = "block", v_mean: str = "global",
+                  v_block: int = 128):
     """fp8 pre-pass for one (b, h).  q, k, v: bf16 bits or exact values [S, D].
 
     Returns a dict with uint8 codes q8, k8, v8 [S, D]; q_scale, k_scale
     [nb] (nb = ceil(S / block)); k_mean [nb or 1, D]; v_mean, v_scale [D]
     (all float32).  ``k_mean`` is "block" (one mean per block of ``block``
     tokens, statistics over the valid tokens only) or "global" (one mean
-    per channel over the whole sequence)."""
+    per channel over the whole sequence).  ``v_mean`` is "global" (v_mean
+    [D]) or "block" (V-Smooth Demean: v_bmean [ceil(S / v_block), D], the
+    bf16-rounded per-channel mean of each block of ``v_block`` tokens, as
+    float32; v_mean is then absent)."""
     q32 = _as_f64(q).astype(np.float32)
     k32 = _as_f64(k).astype(np.float32)
     v32 = _as_f64(v).astype(np.float32)
@@ -173,19 +192,30 @@ def quantize_head(q, k, v, block: int = 64, k_mean: str = "block"):
             out[name + "_scale"][b] = sc
             out[dst][sl] = _codes(src[sl], inv)
     out["k_mean"] = kmean
-    vmean = _mean32(v32, axis=0)
-    vres = (v32 - vmean[None, :]).astype(np.float32)
+    if v_mean == "global":
+        vmean = _mean32(v32, axis=0)
+        vres = (v32 - vmean[None, :]).astype(np.float32)
+        out["v_mean"] = vmean
+    elif v_mean == "block":
+        nbv = -(-S // v_block)
+        vbm = np.empty((nbv, D), np.float32)
+        for b in range(nbv):
+            vbm[b] = bf16_rne(_mean32(v32[b * v_block:(b + 1) * v_block], axis=0))
+        vres = (v32 - np.repeat(vbm, v_block, axis=0)[:S]).astype(np.float32)
+        out["v_bmean"] = vbm
+    else:
+        raise ValueError(v_mean)
     vsc, vinv = _scales(np.max(np.abs(vres), axis=0))
-    out["v_mean"], out["v_scale"] = vmean, vsc
+    out["v_scale"] = vsc
     out["v8"] = _codes(vres, vinv[None, :])
     return out
 
 
-def quantize(q, k, v, block: int = 64, k_mean: str = "block"):
+def quantize(q, k, v, block: int = 64, k_mean: str = "block", v_mean: str = "global"):
     """quantize_head over [B, H, S, D]; arrays gain leading [B, H] axes."""
     q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     B, H = q.shape[:2]
-    parts = [[quantize_head(q[b, h], k[b, h], v[b, h], block, k_mean) for h in range(H)]
+    parts = [[quantize_head(q[b, h], k[b, h], v[b, h], block, k_mean, v_mean) for h in range(H)]
              for b in range(B)]
     return {key: np.stack([np.stack([parts[b][h][key] for h in range(H)]) for b in range(B)])
             for key in parts[0][0]}
@@ -210,7 +240,7 @@ def expcast_byte(log2_v) -> np.ndarray:
 def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
                              p_quant: bool = True, p_scale: float = E4M3_MAX,
                              chunk: int = 256, p_cast: str = "exp",
-                             reference: str | None = None) -> np.ndarray:
+                             reference: str | None = None, v_block: int = 128) -> np.ndarray:
     """Quantisation model of the fp8 attention for one head, in fp64.
 
     Steps: dequantise Q_hat = dec(q8) q_scale, K_hat = dec(k8) k_scale,
@@ -220,6 +250,9 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
     with p_cast="expcast" the E4M3 byte is the ExpCast byte of p_scale p,
     expcast_byte(t - M + log2(p_scale)));
     l_i = sum_j w_ij;  O_i = (sum_j w_ij V_hat_j) / l_i + v_mean.
+    With block means (``v_bmean`` in qz, V-Smooth Demean) the mean is
+    restored per key instead: O_i = sum_j w_ij (V_hat_j + v_bmean_b(j)) / l_i,
+    b(j) = j // v_block (the row sum of each block's weights times its mean).
 
     ``reference`` says which M the weights are taken against: "final" (the
     row maximum, above) or "running", the online softmax's reference: keys
@@ -241,6 +274,12 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
     qh = e4m3_decode(qz["q8"]) * qz["q_scale"].astype(np.float64)[tok_blk][:, None]
     kh = e4m3_decode(qz["k8"]) * qz["k_scale"].astype(np.float64)[tok_blk][:, None]
     vh = e4m3_decode(qz["v8"]) * qz["v_scale"].astype(np.float64)[None, :]
+    if "v_bmean" in qz:
+        vbm = qz["v_bmean"].astype(np.float64)
+        vh = vh + np.repeat(vbm, v_block, axis=0)[:S]
+        vm_add = np.zeros((1, D))
+    else:
+        vm_add = qz["v_mean"].astype(np.float64)[None, :]
     km = qz["k_mean"].astype(np.float64)
     kmean_tok = km[tok_blk] if km.shape[0] == nb and nb > 1 else np.broadcast_to(km[0], (S, D))
     keff = kh + kmean_tok          # q.(k_res + k_mean) = q.k_res + q.k_mean
@@ -273,12 +312,12 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
                 w = weights(tt, M)
                 acc += w @ vh[j0:j0 + block]
                 l += w.sum(axis=1, keepdims=True)
-            out[r0:r0 + chunk] = acc / l + qz["v_mean"].astype(np.float64)[None, :]
+            out[r0:r0 + chunk] = acc / l + vm_add
             continue
         M = np.ceil(t.max(axis=1, keepdims=True))
         w = weights(t, M)
         l = w.sum(axis=1, keepdims=True)
-        out[r0:r0 + chunk] = (w @ vh) / l + qz["v_mean"].astype(np.float64)[None, :]
+        out[r0:r0 + chunk] = (w @ vh) / l + vm_add
     return out
 
 
