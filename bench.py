@@ -240,7 +240,20 @@ def main():
             "expcast_attention_tflops": round(w.flop / (ms_x * 1e-3) / 1e12, 2),
             "expcast_attention_peak_fraction": round(w.flop / (ms_x * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
         }
-        del z, o8
+        log("[bench] fp8 with V-Smooth block means (128-token blocks)")
+        zv = binding.vdit_attn_quant_fp8(q, k, v, v_mean="block")
+        ms_vq = time_launches(lambda: binding.vdit_attn_quant_fp8(q, k, v, out=zv), args.steps, args.warmup)
+        ms_va = time_launches(lambda: binding.vdit_attn_fwd_fp8(zv, scale=scale, o=o8), args.steps, args.warmup)
+        ms_vx = time_launches(lambda: binding.vdit_attn_fwd_fp8(zv, scale=scale, o=o8, expcast=True),
+                              args.steps, args.warmup)
+        result["fp8"].update({
+            "vsmooth_prepass_ms": round(ms_vq, 4),
+            "vsmooth_attention_ms": round(ms_va, 4),
+            "vsmooth_attention_tflops": round(w.flop / (ms_va * 1e-3) / 1e12, 2),
+            "vsmooth_expcast_attention_ms": round(ms_vx, 4),
+            "vsmooth_expcast_attention_tflops": round(w.flop / (ms_vx * 1e-3) / 1e12, 2),
+        })
+        del z, zv, o8
     del o
     torch.cuda.synchronize()
 

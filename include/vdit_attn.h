@@ -168,6 +168,53 @@ vdit_status vdit_attn_fwd_fp8_expcast(const void* q8, const void* k8, const void
                                       void* o, int B, int H, int S, int D, float scale,
                                       void* stream);
 
+/*
+ * V-Smooth with the VC-Attention article's own Demean (section 02): V loses
+ * the per-channel mean of every hardware block of 128 tokens (valid tokens
+ * only) instead of one mean over the sequence; the residual is quantised per
+ * channel in E4M3 with one scale per channel over the sequence.  The mean is
+ * stored in 16 bits (0.125 bit per value element, as the article counts it):
+ *   v_bmean[b,h,d,blk] = bf16_rne(fp32(fp64 sum / n)), blk = token / 128,
+ * and the residual fp32(v - v_bmean) is taken against that rounded mean, so
+ * adding it back restores exactly what was subtracted.
+ * Number of 128-token blocks, padded: nbv_pad = vdit_attn_vsmooth_blocks(S)
+ * = 16 * ceil(ceil(S / 128) / 16); blocks past ceil(S / 128) are written as 0.
+ */
+int vdit_attn_vsmooth_blocks(int S);
+
+/*
+ * The fp8 pre-pass with V block means.  Arguments as vdit_attn_quant_fp8
+ * except:
+ *   v_bmean : [B,H,D,nbv_pad] bf16 (out), channel-major, 16-byte aligned;
+ *   v_scale : [B,H,D] float, per-channel amax/448 of V - v_bmean (out).
+ * The same workspace size (vdit_attn_quant_fp8_workspace_size) suffices.
+ */
+vdit_status vdit_attn_quant_fp8_vsmooth(const void* q, const void* k, const void* v,
+                                        void* q8, void* k8, void* v8,
+                                        float* q_scale, float* k_scale,
+                                        float* k_mean, int k_mean_blocks,
+                                        void* v_bmean, float* v_scale,
+                                        void* workspace, size_t workspace_bytes,
+                                        int B, int H, int S, int D, void* stream);
+
+/*
+ * fp8 attention on the outputs of vdit_attn_quant_fp8_vsmooth.  Scores and
+ * weights as vdit_attn_fwd_fp8 (expcast = 1: ExpCast-FP8 bytes as in
+ * vdit_attn_fwd_fp8_expcast, expcast = 0: exp2 then E4M3); the block means
+ * are restored through the online softmax's row sums (section 02, Restore):
+ *   o = (v_scale * sum_j P8_ij v8_j + sum_blk (sum_{j in blk} P8_ij) v_bmean_blk)
+ *       / (sum_j P8_ij), bf16 out,
+ * with no second pass: each block's weight sum is accumulated per tile and
+ * multiplied into the output every 16 blocks.  expcast other than 0 or 1 is
+ * VDIT_ERR_INVALID_ARG.
+ */
+vdit_status vdit_attn_fwd_fp8_vsmooth(const void* q8, const void* k8, const void* v8,
+                                      const float* q_scale, const float* k_scale,
+                                      const float* k_mean, int k_mean_blocks,
+                                      const void* v_bmean, const float* v_scale,
+                                      void* o, int B, int H, int S, int D, float scale,
+                                      int expcast, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

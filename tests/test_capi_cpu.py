@@ -132,3 +132,21 @@ def test_block_causal_and_expcast_validation():
     assert st == 1 and b"scale" in lib.vdit_last_error()
     st = lib.vdit_attn_fwd_fp8_expcast(A, A, A, A, A, A, 5, A, A, A, 1, 2, 200, 128, 0.1, None)
     assert st == 2 and b"k_mean_blocks" in lib.vdit_last_error()
+
+
+def test_vsmooth_validation():
+    lib = binding.load()
+    assert [lib.vdit_attn_vsmooth_blocks(s) for s in (0, 1, 128, 129, 2048, 2049, 75600)] == \
+        [0, 16, 16, 16, 16, 32, 592]
+    st = lib.vdit_attn_quant_fp8_vsmooth(A, A, A, A, A, A, A, A, A, 4, None, A, A, 1 << 30,
+                                         1, 2, 200, 128, None)
+    assert st == 1 and b"null pointer: v_bmean" in lib.vdit_last_error()
+    st = lib.vdit_attn_quant_fp8_vsmooth(A, A, A, A, A, A, A, A, A, 5, A, A, A, 1 << 30,
+                                         1, 2, 200, 128, None)
+    assert st == 2 and b"k_mean_blocks" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_vsmooth(A, A, A, A, A, A, 4, A, A, A, 1, 2, 200, 128, 0.1, 2, None)
+    assert st == 1 and b"expcast" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_vsmooth(A, A, A, A, A, A, 4, None, A, A, 1, 2, 200, 128, 0.1, 0, None)
+    assert st == 1 and b"null pointer: v_bmean" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_vsmooth(A, A, A, A, A, A, 4, A + 2, A, A, 1, 2, 200, 128, 0.1, 0, None)
+    assert st == 1 and b"aligned: v_bmean" in lib.vdit_last_error()

@@ -1,0 +1,209 @@
+"""GPU parity of the V-Smooth block demean path (VC-Attention article,
+section 02: per-channel means of 128-token hardware blocks, restored through
+the softmax row sums), through the C ABI.
+
+* Pre-pass: codes, scales, K means and the 16-bit V block means equal the
+  oracle's bit for bit; padded block slots are zero.
+* Attention, fed the oracle's quantised tensors, against the fp64
+  quantisation model with block means (exp-then-cast and ExpCast weights):
+  cosine >= 0.999, max-abs <= 5e-2, L1 mean-rel <= 1e-2 against the model
+  rounded to bf16; sizes cross several 16-block restore batches and end in
+  ragged blocks.
+* End to end on the 14B 720p workload against the unquantised truth, within
+  1.5x the error the model itself reaches on the same rows.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as oa
+from oracle import fp8 as ofp8
+from video_diffusion_transformer_vdit_amd import binding, inputs
+
+from gpu_util import (FP8_COS, FP8_MAX_ABS, FP8_MODEL_MEAN_REL, f32_of, log, round_bf16,
+                      sample_rows, tile_v8, to_dev, to_dev_any, untile_v8, workload_heads)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = float(np.float32(1.0 / math.sqrt(128)))
+KEYS = ["q8", "k8", "v8", "q_scale", "k_scale", "k_mean", "v_scale"]
+
+
+def block_offset_bits(shape, seed, spread=1.0, offset_scale=3.0):
+    """Gaussian V plus a per-(128-token block, channel) offset, as bf16 bits."""
+    g = np.random.default_rng(seed)
+    B, H, S, D = shape
+    nbv = -(-S // 128)
+    off = g.standard_normal((B, H, nbv, 1, D)) * offset_scale
+    x = g.standard_normal((B, H, nbv, 128, D)) * spread + off
+    return inputs.f32_to_bf16_bits(x.reshape(B, H, nbv * 128, D)[:, :, :S].astype(np.float32))
+
+
+def rand_bits(shape, seed, scale=1.0, offset=0.0):
+    g = np.random.default_rng(seed)
+    return inputs.f32_to_bf16_bits((g.standard_normal(shape) * scale + offset).astype(np.float32))
+
+
+def gpu_quant(q, k, v, k_mean_blocks=None):
+    import torch
+    z = binding.vdit_attn_quant_fp8(to_dev(q), to_dev(k), to_dev(v), k_mean_blocks=k_mean_blocks,
+                                    v_mean="block")
+    torch.cuda.synchronize()
+    return z
+
+
+def bmean_bits(zg):
+    """GPU v_bmean [B,H,128,nbv_pad] bf16 -> uint16 bits."""
+    import torch
+    return zg["v_bmean"].view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def compare_quant(zg, zo, heads=None, what=""):
+    S = zo["q8"].shape[2]
+    for key in KEYS:
+        g = zg[key].cpu().numpy()
+        if key == "v8":
+            g = untile_v8(g, S)
+        if heads is not None:
+            g = g[:, heads]
+        if not np.array_equal(g, zo[key]):
+            bad = np.argwhere(g != zo[key])
+            raise AssertionError(f"{what} {key}: {len(bad)} mismatches, first at {bad[:3].tolist()}")
+    gb = bmean_bits(zg)
+    if heads is not None:
+        gb = gb[:, heads]
+    nbv = zo["v_bmean"].shape[2]
+    want = (zo["v_bmean"].view(np.uint32) >> 16).astype(np.uint16).transpose(0, 1, 3, 2)
+    assert np.array_equal(gb[..., :nbv], want), f"{what} v_bmean"
+    assert np.all(gb[..., nbv:] == 0), f"{what} v_bmean padding"
+
+
+def zdev(zo):
+    """The oracle's pre-pass outputs on the GPU in the kernel's layouts."""
+    import torch
+    z = {key: to_dev_any(tile_v8(zo[key]) if key == "v8" else zo[key]) for key in KEYS}
+    B, H, nbv, D = zo["v_bmean"].shape
+    nbv_pad = int(binding.load().vdit_attn_vsmooth_blocks(zo["q8"].shape[2]))
+    vb = np.zeros((B, H, D, nbv_pad), np.float32)
+    vb[..., :nbv] = zo["v_bmean"].transpose(0, 1, 3, 2)
+    z["v_bmean"] = torch.from_numpy(vb).to(torch.bfloat16).cuda()  # exact: values are bf16
+    return z
+
+
+def check_model(got, ref, what):
+    ref_b = round_bf16(ref)
+    cos = ofp8.cosine(got, ref_b)
+    ma = ofp8.max_abs(got, ref_b)
+    mr = ofp8.mean_rel_l1(got, ref_b)
+    log(f"{what} vs quant model: cos={cos:.7f} max_abs={ma:.3e} mean_rel={mr:.3e}")
+    assert cos >= FP8_COS and ma <= FP8_MAX_ABS and mr <= FP8_MODEL_MEAN_REL, what
+
+
+def test_block_count():
+    lib = binding.load()
+    assert [lib.vdit_attn_vsmooth_blocks(s) for s in (0, 1, 128, 129, 2048, 2049, 75600)] == \
+        [0, 16, 16, 16, 16, 32, 592]
+
+
+@pytest.mark.parametrize("S", [1, 17, 64, 65, 127, 128, 129, 200, 1000, 2100])
+@pytest.mark.parametrize("mode", ["block", "global"])
+def test_prepass_bit_exact_sweep(S, mode):
+    B, H = 2, 2
+    q, k = rand_bits((B, H, S, 128), 1), rand_bits((B, H, S, 128), 2, 2.0, 0.3)
+    v = block_offset_bits((B, H, S, 128), 3)
+    nb = -(-S // 64)
+    log(f"vsmooth prepass S={S} k_mean={mode}")
+    zg = gpu_quant(q, k, v, nb if mode == "block" else 1)
+    zo = ofp8.quantize(q, k, v, k_mean=mode, v_mean="block")
+    compare_quant(zg, zo, what=f"S={S} {mode}")
+
+
+def test_prepass_constant_blocks():
+    """V constant within every 128-token block: means are the constants,
+    codes decode to zero, scales are one."""
+    B, H, S = 1, 2, 300
+    g = np.random.default_rng(7)
+    c = np.round(g.standard_normal((B, H, 3, 1, 128)) * 16) / 8
+    v = inputs.f32_to_bf16_bits(np.broadcast_to(c, (B, H, 3, 128, 128)).reshape(B, H, 384, 128)[:, :, :S]
+                                .astype(np.float32))
+    q, k = rand_bits((B, H, S, 128), 8), rand_bits((B, H, S, 128), 9)
+    zg = gpu_quant(q, k, v)
+    zo = ofp8.quantize(q, k, v, v_mean="block")
+    compare_quant(zg, zo, what="constant blocks")
+    assert np.all(ofp8.e4m3_decode(zo["v8"]) == 0) and np.all(zg["v_scale"].cpu().numpy() == 1.0)
+
+
+def test_prepass_bit_exact_workload():
+    import torch
+    w = inputs.get_workload("wan2.1-14b-720p-fp8")
+    log("vsmooth prepass 720p: generating")
+    q, k, v = inputs.make_inputs(w)
+    heads = workload_heads(w.H)
+    zg = gpu_quant(q, k, v)
+    log(f"vsmooth prepass 720p: oracle on heads {heads}")
+    zo = ofp8.quantize(q[:, heads], k[:, heads], v[:, heads], v_mean="block")
+    compare_quant(zg, zo, heads, "720p")
+    del zg
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("expcast", [False, True])
+@pytest.mark.parametrize("S,seed", [(1, 1), (63, 2), (128, 3), (129, 4), (1000, 5), (2100, 6), (4200, 7)])
+def test_attention_vs_quant_model_sweep(S, seed, expcast):
+    """S = 2100 and 4200 cross one and two 16-block restore batches and end in
+    ragged 128-token blocks."""
+    import torch
+    B, H = 1, 2
+    q, k = rand_bits((B, H, S, 128), seed), rand_bits((B, H, S, 128), seed + 10, 1.0, 0.5)
+    v = block_offset_bits((B, H, S, 128), seed + 20)
+    zo = ofp8.quantize(q, k, v, v_mean="block")
+    log(f"vsmooth attention S={S} expcast={expcast}")
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE, expcast=expcast)
+    torch.cuda.synchronize()
+    got = f32_of(o)
+    ref = ofp8.attention_fp8_model(zo, SCALE, p_cast="expcast" if expcast else "exp")
+    check_model(got, ref, f"vsmooth S={S} expcast={expcast}")
+
+
+def test_attention_global_k_mean():
+    import torch
+    B, H, S = 1, 2, 1500
+    q, k = rand_bits((B, H, S, 128), 41), rand_bits((B, H, S, 128), 42, 1.0, 0.5)
+    v = block_offset_bits((B, H, S, 128), 43)
+    zo = ofp8.quantize(q, k, v, k_mean="global", v_mean="block")
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE)
+    torch.cuda.synchronize()
+    check_model(f32_of(o), ofp8.attention_fp8_model(zo, SCALE), "vsmooth global K mean")
+
+
+@pytest.mark.parametrize("expcast", [False, True])
+def test_workload_vs_model_and_truth(expcast):
+    """Full-size 720p launch, GPU pre-pass + GPU attention: against the model
+    with block means on sampled rows, and against the truth within 1.5x the
+    model's own error there."""
+    import torch
+    w = inputs.get_workload("wan2.1-14b-720p-fp8")
+    q, k, v = inputs.make_inputs(w)
+    log(f"vsmooth 720p expcast={expcast}: GPU pre-pass + attention")
+    z = gpu_quant(q, k, v)
+    o = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=expcast)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.S, n_random=32)
+    heads = workload_heads(w.H)[:2]
+    got = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+    del o, z
+    torch.cuda.empty_cache()
+    for i, h in enumerate(heads):
+        zh = ofp8.quantize_head(q[0, h], k[0, h], v[0, h], v_mean="block")
+        model = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows,
+                                              p_cast="expcast" if expcast else "exp")
+        check_model(got[i], model, f"vsmooth 720p head {h} expcast={expcast}")
+        truth = oa.attention_head(q[0, h], k[0, h], v[0, h], SCALE, rows=rows)
+        fl_cos, fl_ma = ofp8.cosine(model, truth), ofp8.max_abs(model, truth)
+        cos, ma = ofp8.cosine(got[i], truth), ofp8.max_abs(got[i], truth)
+        log(f"vsmooth 720p head {h} vs truth: gpu cos={cos:.6f} max_abs={ma:.3e} | "
+            f"model floor cos={fl_cos:.6f} max_abs={fl_ma:.3e}")
+        assert 1 - cos <= 1.5 * (1 - fl_cos) + 1e-5
+        assert ma <= 1.5 * fl_ma + 1e-3

@@ -32,6 +32,11 @@ SIGNATURES = {
     "vdit_attn_quant_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "vdit_attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
     "vdit_attn_fwd_fp8_expcast": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
+    "vdit_attn_quant_fp8_vsmooth": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _Z,
+                                         _I, _I, _I, _I, _P]),
+    "vdit_attn_vsmooth_blocks": (_I, [_I]),
+    "vdit_attn_fwd_fp8_vsmooth": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F,
+                                       _I, _P]),
 }
 
 _lib = None
@@ -126,8 +131,11 @@ def vdit_attn_fwd_block_causal(q, k, v, chunk, o=None, scale=None, stream=None):
     return o
 
 
-def quant_buffers(B, H, S, k_mean_blocks=None, device="cuda"):
-    """Allocate the pre-pass outputs and workspace (torch, on ``device``)."""
+def quant_buffers(B, H, S, k_mean_blocks=None, device="cuda", v_mean="global"):
+    """Allocate the pre-pass outputs and workspace (torch, on ``device``).
+    ``v_mean="block"`` (V-Smooth Demean) replaces v_mean [B,H,128] by v_bmean,
+    bf16 [B,H,128,nbv_pad]: per channel the mean of every 128-token block,
+    nbv_pad = vdit_attn_vsmooth_blocks(S) (zero padded)."""
     import torch
     nb = -(-S // FP8_BLOCK)
     kmb = nb if k_mean_blocks is None else int(k_mean_blocks)
@@ -137,7 +145,7 @@ def quant_buffers(B, H, S, k_mean_blocks=None, device="cuda"):
         raise ValueError("invalid shape or k_mean_blocks for the fp8 pre-pass")
     f32 = dict(dtype=torch.float32, device=device)
     u8 = dict(dtype=torch.uint8, device=device)
-    return {
+    z = {
         "q8": torch.empty((B, H, S, HEAD_DIM), **u8),
         "k8": torch.empty((B, H, S, HEAD_DIM), **u8),
         # V codes in the attention kernel's layout: per 64-token block a
@@ -146,21 +154,41 @@ def quant_buffers(B, H, S, k_mean_blocks=None, device="cuda"):
         "q_scale": torch.empty((B, H, nb), **f32),
         "k_scale": torch.empty((B, H, nb), **f32),
         "k_mean": torch.empty((B, H, kmb, HEAD_DIM), **f32),
-        "v_mean": torch.empty((B, H, HEAD_DIM), **f32),
         "v_scale": torch.empty((B, H, HEAD_DIM), **f32),
         "workspace": torch.empty(ws, **u8),
     }
+    if v_mean == "global":
+        z["v_mean"] = torch.empty((B, H, HEAD_DIM), **f32)
+    elif v_mean == "block":
+        nbv_pad = int(lib.vdit_attn_vsmooth_blocks(S))
+        z["v_bmean"] = torch.empty((B, H, HEAD_DIM, nbv_pad), dtype=torch.bfloat16, device=device)
+    else:
+        raise ValueError(f"v_mean must be 'global' or 'block', not {v_mean!r}")
+    return z
 
 
-def vdit_attn_quant_fp8(q, k, v, k_mean_blocks=None, out=None, stream=None):
-    """fp8 pre-pass on bf16 q, k, v; returns the dict of quant_buffers()."""
+def vdit_attn_quant_fp8(q, k, v, k_mean_blocks=None, out=None, stream=None, v_mean="global"):
+    """fp8 pre-pass on bf16 q, k, v; returns the dict of quant_buffers().
+    With ``v_mean="block"`` (or an ``out`` holding v_bmean) V is smoothed by
+    its 128-token block means (vdit_attn_quant_fp8_vsmooth)."""
     import torch
     B, H, S, D = _shape4(q)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
-    z = quant_buffers(B, H, S, k_mean_blocks, q.device) if out is None else out
+    z = quant_buffers(B, H, S, k_mean_blocks, q.device, v_mean) if out is None else out
     kmb = int(z["k_mean"].shape[2])
     lib = load()
+    if "v_bmean" in z:
+        check(lib.vdit_attn_quant_fp8_vsmooth(
+            _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+            _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),
+            _dev(z["v8"], torch.uint8, "v8"), _dev(z["q_scale"], torch.float32, "q_scale"),
+            _dev(z["k_scale"], torch.float32, "k_scale"), _dev(z["k_mean"], torch.float32, "k_mean"),
+            kmb, _dev(z["v_bmean"], torch.bfloat16, "v_bmean"),
+            _dev(z["v_scale"], torch.float32, "v_scale"),
+            _dev(z["workspace"], torch.uint8, "workspace"), z["workspace"].numel(),
+            B, H, S, D, _stream(stream)))
+        return z
     check(lib.vdit_attn_quant_fp8(
         _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
         _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),
@@ -175,7 +203,8 @@ def vdit_attn_quant_fp8(q, k, v, k_mean_blocks=None, out=None, stream=None):
 def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False):
     """fp8 attention on pre-pass outputs ``z`` (dict as from vdit_attn_quant_fp8);
     returns bf16 o [B, H, S, 128].  ``expcast`` selects the ExpCast-FP8 entry
-    point (P bytes written directly from the log domain)."""
+    point (P bytes written directly from the log domain).  A ``z`` holding
+    v_bmean (V block means) goes to vdit_attn_fwd_fp8_vsmooth."""
     import torch
     B, H, S, D = _shape4(z["q8"])
     if o is None:
@@ -183,6 +212,15 @@ def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False):
     scale = D ** -0.5 if scale is None else float(scale)
     kmb = int(z["k_mean"].shape[2])
     lib = load()
+    if "v_bmean" in z:
+        check(lib.vdit_attn_fwd_fp8_vsmooth(
+            _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),
+            _dev(z["v8"], torch.uint8, "v8"), _dev(z["q_scale"], torch.float32, "q_scale"),
+            _dev(z["k_scale"], torch.float32, "k_scale"), _dev(z["k_mean"], torch.float32, "k_mean"),
+            kmb, _dev(z["v_bmean"], torch.bfloat16, "v_bmean"),
+            _dev(z["v_scale"], torch.float32, "v_scale"),
+            _dev(o, torch.bfloat16, "o"), B, H, S, D, scale, 1 if expcast else 0, _stream(stream)))
+        return o
     fn = lib.vdit_attn_fwd_fp8_expcast if expcast else lib.vdit_attn_fwd_fp8
     check(fn(
         _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),

@@ -26,6 +26,16 @@
 // restore is exact.  Epilogue: o = v_scale (sum_j P8_ij v8_j) / (sum_j P8_ij)
 // + v_mean.
 //
+// With V block means (the article's Demean over 128-token hardware blocks)
+// the restore runs inside the key loop instead: the row-sum MFMA uses a
+// one-hot operand whose single row of ones is the block's slot, so it
+// accumulates each block's weight sum in its own row (16 blocks = 32 tiles
+// per batch); after each batch two bf16 MFMAs per 32 channels (the exact
+// bf16 means against the high and low bf16 parts of the sums, about 2^-16
+// relative) give sum_b (sum_{j in b} P8_ij) v_mean_b, which is added to the
+// code-unit accumulator divided by v_scale, and the batch's sums join the
+// row sum.  Epilogue: o = v_scale acc / l.
+//
 // Work layout (the bf16 kernel's): one workgroup = 8 waves x 32 queries, one
 // workgroup per CU; scores transposed (S^T = K Q^T) so each lane owns one
 // query; K tiles (row-major, 16-byte chunks XOR-swizzled by key & 7) and V
@@ -76,13 +86,15 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 
 // kBlockMean: one K mean per 64-token block (else one mean per head);
 // kExpCast: P8 bytes written directly from the log domain (else exp2, then
-// an E4M3 conversion)
-template <bool kBlockMean, bool kExpCast>
+// an E4M3 conversion); kVBlock: V means per 128-token block (v_bmean, bf16,
+// [bh][channel][nbv_pad]) restored in the loop (else one v_mean per channel)
+template <bool kBlockMean, bool kExpCast, bool kVBlock>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const float* __restrict__ k_mean, const float* __restrict__ v_mean,
-    const float* __restrict__ v_scale, uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
+    const uint16_t* __restrict__ v_bmean, int nbv_pad, const float* __restrict__ v_scale,
+    uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
   // three-deep rings of K and V tiles, one LDS object per buffer
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
@@ -91,6 +103,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) char lds_v1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v2[kTileBytes];
   __shared__ float lds_comp[kWaves][kCompBlocks][32];
+  __shared__ __attribute__((aligned(16))) float lds_ivs[kHeadDim];  // 1 / v_scale (V block means only)
+  __shared__ bf16x8 lds_qh[kWaves][8][64];  // dec(q8) in bf16, per lane (K-mean term)
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
@@ -153,14 +167,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const float qsc = q_scale[(size_t)bh * nkt + min(qrow, S - 1) / kBc] * c;
 
   // dec(q8) in bf16 (exact) as the B operand of the K-mean MFMAs (lane:
-  // query col, channels 16kk + 8half .. +7).
-  bf16x8 qh[8];
+  // query col, channels 16kk + 8half .. +7).  With V block means it is parked
+  // in LDS (needed once per 32 tiles, it would hold 32 registers that the
+  // restore needs); otherwise it stays in registers.
+  bf16x8 qh_reg[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const uint8_t* p = Q8h + (size_t)qrow * kHeadDim + 16 * kk + 8 * half;
     const u32x2 w = qok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qh[kk][e] = (__bf16)e4m3_value((w[e >> 2] >> (8 * (e & 3))) & 255u);
+    for (int e = 0; e < 8; ++e) qh_reg[kk][e] = (__bf16)e4m3_value((w[e >> 2] >> (8 * (e & 3))) & 255u);
+    if (kVBlock) lds_qh[wave][kk][lane] = qh_reg[kk];
   }
   const int nbm = kBlockMean ? nkt : 1;
   const float* kmh = k_mean + (size_t)bh * nbm * kHeadDim;
@@ -184,8 +201,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
         hi[e] = (__bf16)x;
         lo[e] = (__bf16)(x - (float)hi[e]);
       }
-      cm = mfma32x32x16_bf16(hi, qh[kk], cm);
-      cm = mfma32x32x16_bf16(lo, qh[kk], cm);
+      const bf16x8 qh = kVBlock ? lds_qh[wave][kk][lane] : qh_reg[kk];
+      cm = mfma32x32x16_bf16(hi, qh, cm);
+      cm = mfma32x32x16_bf16(lo, qh, cm);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) lds_comp[wave][8 * (i >> 2) + 4 * half + (i & 3)][col] = cm[i];
@@ -236,6 +254,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
   float m_ref = -INFINITY;
+  // V block means: row sum of the drained batches; 1 / v_scale per channel
+  // in LDS (it scales the means into code units for the restore MFMA)
+  float l_tot = 0.f;
+  const uint16_t* vbmh = v_bmean + (size_t)bh * kHeadDim * nbv_pad;
+  if (kVBlock && tid < kHeadDim) lds_ivs[tid] = 1.0f / v_scale[(size_t)bh * kHeadDim + tid];
+  // Restore of batch `batch` (128-token blocks 16 batch .. +15): lane (query
+  // col, half) holds the weight sums of blocks 16 batch + 8 half + j in
+  // lacc[j] (the one-hot rows below put them there), which is exactly the B
+  // operand of a 32x32x16 bf16 MFMA over those 16 blocks.
+  // The batch's means (16 bytes per lane and 32-channel block) are loaded in
+  // the exponential phase before the drain, so their latency overlaps it.
+  u32x4 vbm_pre[4];
+  auto vload = [&](int batch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      vbm_pre[mb] = *reinterpret_cast<const u32x4*>(vbmh + (size_t)(32 * mb + col) * nbv_pad +
+                                                     16 * batch + 8 * half);
+  };
+  auto vdrain = [&]() __attribute__((always_inline)) {
+    bf16x8 bhi, blo;
+    float ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ls += lacc[j];
+      bhi[j] = (__bf16)lacc[j];
+      blo[j] = (__bf16)(lacc[j] - (float)bhi[j]);
+    }
+    l_tot += sum_halves(ls);
+    // r = means x sums in value units (the bf16 means are exact operands),
+    // then acc += r / v_scale row by row
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const bf16x8 vm = __builtin_bit_cast(bf16x8, vbm_pre[mb]);
+      f32x16 r;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] = 0.f;
+      r = mfma32x32x16_bf16(vm, bhi, r);
+      r = mfma32x32x16_bf16(vm, blo, r);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 iv = *reinterpret_cast<const f32x4*>(&lds_ivs[32 * mb + 8 * g + 4 * half]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mb][4 * g + e] = fmaf(r[4 * g + e], iv[e], acc[mb][4 * g + e]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
+  };
 
   // P8 of tile t: t = a dot + cb in the log2 domain (a >= 0, so the row max
   // of t is at the row max of dot); reference update and (rare) rescale;
@@ -259,6 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       const float mnext = mq > m_ref ? ceilf(mq) : m_ref;
       const float alpha = exp2_fast(m_ref - mnext);
       lacc *= alpha;
+      if (kVBlock) l_tot *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
       m_ref = mnext;
@@ -293,7 +360,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     }
   };
   // O^T += V^T P^T (one 32x32x64 MFMA per 32-channel block) and the row sum
-  auto pv = [&](const char* Vb) __attribute__((always_inline)) {
+  // (with V block means: the weight sum of tile t's 128-token block, in the
+  // output row of its slot k = (t / 2) % 16, row 4(k / 8) + 8((k % 8) / 4) +
+  // k % 4, which lane (query, k / 8) holds in lacc[k % 8])
+  auto pv = [&](const char* Vb, int t) __attribute__((always_inline)) {
     const i32x8 pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3],
                       (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
 #pragma unroll
@@ -303,7 +373,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
                             *reinterpret_cast<const u32x4*>(p + voff[1]));
       acc[mb] = mfma32x32x64_fp8(av, pb, acc[mb]);
     }
-    lacc = mfma32x32x64_fp8(ones, pb, lacc);
+    if (kVBlock) {
+      const int k = (t >> 1) & 15;
+      const int r = 4 * (k >> 3) + 8 * ((k & 7) >> 2) + (k & 3);
+      const int o = col == r ? 0x38383838 : 0;
+      const i32x8 onehot = {o, o, o, o, o, o, o, o};
+      lacc = mfma32x32x64_fp8(onehot, pb, lacc);
+    } else {
+      lacc = mfma32x32x64_fp8(ones, pb, lacc);
+    }
   };
 
   // workgroup barrier that the compiler moves no memory access across
@@ -323,6 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // two loads before each barrier.
   const bool group_a = wave < 4;
   auto phase1 = [&](int t) __attribute__((always_inline)) {
+    if (kVBlock && (t % 32) == 0 && t > 0) vload((t >> 5) - 1);
     softmax_p(t);
     // consume P here: otherwise the exponentials are moved to their use
     // after the barrier, into the MFMA phase
@@ -334,11 +413,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   };
   auto phase2 = [&](int t, const char* kn, const char* vc, const void* kfill, const void* vfill)
                     __attribute__((always_inline)) {
+    // batch t/32 - 1 is complete (its last P.V ran in the previous phase 2)
+    if (kVBlock && (t % 32) == 0 && t > 0) {
+      vdrain();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     issue_k(t + 3, kfill);
     issue_v(t + 2, vfill);
     __builtin_amdgcn_sched_barrier(0);
     qk(kn);
-    pv(vc);
+    pv(vc, t);
     // keys past S (the ragged last tile, or the tile after the last, whose
     // scores come from reloaded data and must weigh nothing)
     if ((t + 1) * kBc + kBc > S) mask_tail(t + 1);
@@ -383,8 +467,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  const float inv = 1.0f / lacc[0];
-  if (qok) {
+  if (kVBlock) {
+    vload((nkt - 1) >> 5);
+    vdrain();
+  }
+  const float inv = 1.0f / (kVBlock ? l_tot : lacc[0]);
+  if (qok && kVBlock) {
+    const float* vsh = v_scale + (size_t)bh * kHeadDim;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * mb + 8 * g + 4 * half;
+        const f32x4 vs = *reinterpret_cast<const f32x4*>(vsh + d0);
+        u32x2 w;
+        w.x = pack_bf16x2(acc[mb][4 * g] * inv * vs[0], acc[mb][4 * g + 1] * inv * vs[1]);
+        w.y = pack_bf16x2(acc[mb][4 * g + 2] * inv * vs[2], acc[mb][4 * g + 3] * inv * vs[3]);
+        *reinterpret_cast<u32x2*>(Oh + (size_t)qrow * kHeadDim + d0) = w;
+      }
+  } else if (qok) {
     const float* vsh = v_scale + (size_t)bh * kHeadDim;
     const float* vmh = v_mean + (size_t)bh * kHeadDim;
 #pragma unroll
@@ -404,27 +505,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   }
 }
 
-template <bool kExpCast>
+template <bool kExpCast, bool kVBlock>
 void launch_fp8(bool block_mean, unsigned blocks, hipStream_t stream, const uint8_t* q,
                 const uint8_t* k, const uint8_t* v, const float* q_scale, const float* k_scale,
-                const float* k_mean, const float* v_mean, const float* v_scale, uint16_t* out,
-                int S, int n_qtiles, float c) {
+                const float* k_mean, const float* v_mean, const uint16_t* v_bmean, int nbv_pad,
+                const float* v_scale, uint16_t* out, int S, int n_qtiles, float c) {
   if (block_mean)
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, kExpCast>), dim3(blocks), dim3(kThreads), 0, stream,
-                       q, k, v, q_scale, k_scale, k_mean, v_mean, v_scale, out, S, n_qtiles, c);
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, kExpCast, kVBlock>), dim3(blocks), dim3(kThreads),
+                       0, stream, q, k, v, q_scale, k_scale, k_mean, v_mean, v_bmean, nbv_pad,
+                       v_scale, out, S, n_qtiles, c);
   else
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, kExpCast>), dim3(blocks), dim3(kThreads), 0,
-                       stream, q, k, v, q_scale, k_scale, k_mean, v_mean, v_scale, out, S, n_qtiles,
-                       c);
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, kExpCast, kVBlock>), dim3(blocks),
+                       dim3(kThreads), 0, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
+                       v_bmean, nbv_pad, v_scale, out, S, n_qtiles, c);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                const float* q_scale, const float* k_scale, const float* k_mean,
-                               int k_mean_blocks, const float* v_mean, const float* v_scale,
-                               void* o, int B, int H, int S, float scale, bool expcast,
-                               hipStream_t stream) {
+                               int k_mean_blocks, const float* v_mean, const void* v_bmean,
+                               const float* v_scale, void* o, int B, int H, int S, float scale,
+                               bool expcast, hipStream_t stream) {
   const int n_qtiles = (S + kBr - 1) / kBr;
   const unsigned blocks = (unsigned)((long long)B * H * n_qtiles);
   const int nb = (S + kBc - 1) / kBc;
@@ -434,12 +536,23 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
   const uint8_t* v = static_cast<const uint8_t*>(v8);
   uint16_t* out = static_cast<uint16_t*>(o);
   const float c = scale * kLog2e;
-  if (expcast)
-    launch_fp8<true>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean, v_scale,
-                     out, S, n_qtiles, c);
-  else
-    launch_fp8<false>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean, v_scale,
-                      out, S, n_qtiles, c);
+  const uint16_t* vbm = static_cast<const uint16_t*>(v_bmean);
+  const int nbv_pad = vsmooth_blocks_padded(S);
+  if (vbm) {
+    if (expcast)
+      launch_fp8<true, true>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
+                             vbm, nbv_pad, v_scale, out, S, n_qtiles, c);
+    else
+      launch_fp8<false, true>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
+                              vbm, nbv_pad, v_scale, out, S, n_qtiles, c);
+  } else {
+    if (expcast)
+      launch_fp8<true, false>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
+                              vbm, nbv_pad, v_scale, out, S, n_qtiles, c);
+    else
+      launch_fp8<false, false>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean,
+                               v_mean, vbm, nbv_pad, v_scale, out, S, n_qtiles, c);
+  }
   return hipGetLastError();
 }
 

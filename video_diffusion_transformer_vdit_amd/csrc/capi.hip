@@ -107,11 +107,11 @@ vdit_status vdit_attn_fwd_block_causal(const void* q, const void* k, const void*
   return fwd_bf16(q, k, v, o, B, H, S, D, scale, chunk, dtype, stream);
 }
 
-vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v, void* q8, void* k8,
-                                void* v8, float* q_scale, float* k_scale, float* k_mean,
-                                int k_mean_blocks, float* v_mean, float* v_scale, void* workspace,
-                                size_t workspace_bytes, int B, int H, int S, int D,
-                                void* stream) {
+static vdit_status quant_fp8(const void* q, const void* k, const void* v, void* q8, void* k8,
+                             void* v8, float* q_scale, float* k_scale, float* k_mean,
+                             int k_mean_blocks, float* v_mean, void* v_bmean, float* v_scale,
+                             void* workspace, size_t workspace_bytes, int B, int H, int S, int D,
+                             void* stream) {
   VDIT_TRY(check_ptr(q, "q"));
   VDIT_TRY(check_ptr(k, "k"));
   VDIT_TRY(check_ptr(v, "v"));
@@ -121,7 +121,10 @@ vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v, voi
   VDIT_TRY(check_fptr(q_scale, "q_scale"));
   VDIT_TRY(check_fptr(k_scale, "k_scale"));
   VDIT_TRY(check_fptr(k_mean, "k_mean"));
-  VDIT_TRY(check_fptr(v_mean, "v_mean"));
+  if (v_bmean)
+    VDIT_TRY(check_ptr(v_bmean, "v_bmean"));
+  else
+    VDIT_TRY(check_fptr(v_mean, "v_mean"));
   VDIT_TRY(check_fptr(v_scale, "v_scale"));
   VDIT_TRY(check_ptr(workspace, "workspace"));
   VDIT_TRY(check_shape(B, H, S, D));
@@ -131,8 +134,33 @@ vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v, voi
   if (workspace_bytes < vdit::quant_fp8_workspace_bytes(B, H, S, k_mean_blocks))
     return fail(VDIT_ERR_INVALID_ARG, "%s", "workspace too small");
   return hip_result(vdit::launch_quant_fp8(q, k, v, q8, k8, v8, q_scale, k_scale, k_mean,
-                                           k_mean_blocks, v_mean, v_scale, workspace, B, H, S,
-                                           static_cast<hipStream_t>(stream)));
+                                           k_mean_blocks, v_mean, v_bmean, v_scale, workspace, B,
+                                           H, S, static_cast<hipStream_t>(stream)));
+}
+
+vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v, void* q8, void* k8,
+                                void* v8, float* q_scale, float* k_scale, float* k_mean,
+                                int k_mean_blocks, float* v_mean, float* v_scale, void* workspace,
+                                size_t workspace_bytes, int B, int H, int S, int D,
+                                void* stream) {
+  if (!v_mean) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: v_mean");
+  return quant_fp8(q, k, v, q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, nullptr,
+                   v_scale, workspace, workspace_bytes, B, H, S, D, stream);
+}
+
+vdit_status vdit_attn_quant_fp8_vsmooth(const void* q, const void* k, const void* v, void* q8,
+                                        void* k8, void* v8, float* q_scale, float* k_scale,
+                                        float* k_mean, int k_mean_blocks, void* v_bmean,
+                                        float* v_scale, void* workspace, size_t workspace_bytes,
+                                        int B, int H, int S, int D, void* stream) {
+  if (!v_bmean) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: v_bmean");
+  return quant_fp8(q, k, v, q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, nullptr, v_bmean,
+                   v_scale, workspace, workspace_bytes, B, H, S, D, stream);
+}
+
+int vdit_attn_vsmooth_blocks(int S) {
+  if (S < 1) return 0;
+  return vdit::vsmooth_blocks_padded(S);
 }
 
 size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean_blocks) {
@@ -144,15 +172,19 @@ size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean
 
 static vdit_status fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
                            const float* k_scale, const float* k_mean, int k_mean_blocks,
-                           const float* v_mean, const float* v_scale, void* o, int B, int H, int S,
-                           int D, float scale, bool expcast, void* stream) {
+                           const float* v_mean, const void* v_bmean, const float* v_scale,
+                           void* o, int B, int H, int S, int D, float scale, bool expcast,
+                           void* stream) {
   VDIT_TRY(check_ptr(q8, "q8"));
   VDIT_TRY(check_ptr(k8, "k8"));
   VDIT_TRY(check_ptr(v8, "v8"));
   VDIT_TRY(check_fptr(q_scale, "q_scale"));
   VDIT_TRY(check_fptr(k_scale, "k_scale"));
   VDIT_TRY(check_fptr(k_mean, "k_mean"));
-  VDIT_TRY(check_fptr(v_mean, "v_mean"));
+  if (v_bmean)
+    VDIT_TRY(check_ptr(v_bmean, "v_bmean"));
+  else
+    VDIT_TRY(check_fptr(v_mean, "v_mean"));
   VDIT_TRY(check_fptr(v_scale, "v_scale"));
   VDIT_TRY(check_ptr(o, "o"));
   VDIT_TRY(check_shape(B, H, S, D));
@@ -161,7 +193,7 @@ static vdit_status fwd_fp8(const void* q8, const void* k8, const void* v8, const
   if (k_mean_blocks != 1 && k_mean_blocks != nb)
     return fail(VDIT_ERR_UNSUPPORTED, "%s", "k_mean_blocks must be 1 or ceil(S/64)");
   return hip_result(vdit::launch_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks,
-                                              v_mean, v_scale, o, B, H, S, scale, expcast,
+                                              v_mean, v_bmean, v_scale, o, B, H, S, scale, expcast,
                                               static_cast<hipStream_t>(stream)));
 }
 
@@ -169,8 +201,9 @@ vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                               const float* q_scale, const float* k_scale, const float* k_mean,
                               int k_mean_blocks, const float* v_mean, const float* v_scale,
                               void* o, int B, int H, int S, int D, float scale, void* stream) {
-  return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, v_scale, o, B, H, S,
-                 D, scale, false, stream);
+  if (!v_mean) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: v_mean");
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, nullptr, v_scale, o,
+                 B, H, S, D, scale, false, stream);
 }
 
 vdit_status vdit_attn_fwd_fp8_expcast(const void* q8, const void* k8, const void* v8,
@@ -178,8 +211,20 @@ vdit_status vdit_attn_fwd_fp8_expcast(const void* q8, const void* k8, const void
                                       const float* k_mean, int k_mean_blocks, const float* v_mean,
                                       const float* v_scale, void* o, int B, int H, int S, int D,
                                       float scale, void* stream) {
-  return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, v_scale, o, B, H, S,
-                 D, scale, true, stream);
+  if (!v_mean) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: v_mean");
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, nullptr, v_scale, o,
+                 B, H, S, D, scale, true, stream);
+}
+
+vdit_status vdit_attn_fwd_fp8_vsmooth(const void* q8, const void* k8, const void* v8,
+                                      const float* q_scale, const float* k_scale,
+                                      const float* k_mean, int k_mean_blocks, const void* v_bmean,
+                                      const float* v_scale, void* o, int B, int H, int S, int D,
+                                      float scale, int expcast, void* stream) {
+  if (!v_bmean) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: v_bmean");
+  if (expcast != 0 && expcast != 1) return fail(VDIT_ERR_INVALID_ARG, "%s", "expcast must be 0 or 1");
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, nullptr, v_bmean, v_scale, o,
+                 B, H, S, D, scale, expcast == 1, stream);
 }
 
 }  // extern "C"

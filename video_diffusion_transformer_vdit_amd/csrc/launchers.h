@@ -11,16 +11,25 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
 
 size_t quant_fp8_workspace_bytes(int B, int H, int S, int k_mean_blocks);
 
+// V-Smooth block means: one per channel and 128-token block, stored
+// [b,h][channel][block] with the block count padded to a multiple of 16.
+constexpr int kVSmoothBlock = 128;
+inline int vsmooth_blocks_padded(int S) {
+  const int nbv = (S + kVSmoothBlock - 1) / kVSmoothBlock;
+  return (nbv + 15) / 16 * 16;
+}
+
 hipError_t launch_quant_fp8(const void* q, const void* k, const void* v,
                             void* q8, void* k8, void* v8, float* q_scale, float* k_scale,
-                            float* k_mean, int k_mean_blocks, float* v_mean, float* v_scale,
-                            void* workspace, int B, int H, int S, hipStream_t stream);
+                            float* k_mean, int k_mean_blocks, float* v_mean, void* v_bmean,
+                            float* v_scale, void* workspace, int B, int H, int S,
+                            hipStream_t stream);
 
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                const float* q_scale, const float* k_scale,
                                const float* k_mean, int k_mean_blocks,
-                               const float* v_mean, const float* v_scale, void* o,
-                               int B, int H, int S, float scale, bool expcast,
-                               hipStream_t stream);
+                               const float* v_mean, const void* v_bmean,
+                               const float* v_scale, void* o, int B, int H, int S, float scale,
+                               bool expcast, hipStream_t stream);
 
 }  // namespace vdit

@@ -15,6 +15,16 @@
 //      1/scale (workspace), k_mean (global mode)
 //   3. per (b,h, block): V residual codes; K residual codes (global mode)
 //
+// With block means for V (the article's own Demean: one mean per channel
+// and hardware block of 128 tokens) launch 2 forms, per 128-token block, the
+// mean from the two 64-token partial sums, rounds it to bf16 (the 16-bit
+// mean: 0.125 bit per value element) and the block's residual range from its
+// minima and maxima; the per-channel scale covers the residual over the whole
+// sequence.  Launch 3 subtracts each token's block mean.  The means are
+// written channel-major, [b,h][channel][block], padded with zeros to a
+// multiple of 16 blocks: the attention kernel restores them 16 blocks at a
+// time.
+//
 // V codes are written as the attention kernel reads them: per (b,h) and
 // 64-token block one 8 KB tile of 128 channel rows x 64 key slots, slot s of
 // a row holding key 32((s>>4)&1) + 8((s>>2)&3) + 4(s>>5) + (s&3) of the block
@@ -26,7 +36,9 @@
 // checked bit for bit: sums of bf16 values in fp64 (exact for these inputs),
 // mean = fp32(sum / n), residual = fp32(x - mean), scale = fp32(amax / 448)
 // and inv = fp32(448 / amax) from fp64 quotients (1 and 0 when amax = 0),
-// code = E4M3 round-to-nearest-even of clamp(fp32(r * inv), +-448).
+// code = E4M3 round-to-nearest-even of clamp(fp32(r * inv), +-448); the
+// 16-bit V block mean is bf16(fp32 mean), nearest even, and the residual is
+// taken against it.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -80,6 +92,12 @@ __device__ __forceinline__ u32x2 encode8(const float* f, float inv) {
   r.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
   r.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
   return r;
+}
+
+// float -> bf16 bits, round to nearest even (finite values)
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -259,9 +277,12 @@ __global__ __launch_bounds__(kThreads) void quant_blocks_kernel(
 }
 
 // Launch 2: one workgroup per bh; thread t < 128 owns channel t.
+// With v_bmean (block mode) thread (d, part) handles the 128-token blocks of
+// parity part: mean, its bf16 rounding, and the block's residual range.
 __global__ __launch_bounds__(kThreads) void quant_reduce_kernel(
     float* __restrict__ v_mean, float* __restrict__ v_scale, float* __restrict__ k_mean,
-    Workspace ws, int S, int nb, int k_global) {
+    uint16_t* __restrict__ v_bmean, int nbv_pad, Workspace ws, int S, int nb, int k_global) {
+  __shared__ float ram[2][kHeadDim];
   __shared__ double rs[2][kHeadDim];
   __shared__ double rk[2][kHeadDim];
   __shared__ float rmn[2][kHeadDim], rmx[2][kHeadDim];
@@ -280,8 +301,36 @@ __global__ __launch_bounds__(kThreads) void quant_reduce_kernel(
   rk[part][d] = sk;
   rmn[part][d] = mn;
   rmx[part][d] = mx;
+  if (v_bmean) {
+    const int nbv = (S + 2 * kBlock - 1) / (2 * kBlock);
+    uint16_t* vb = v_bmean + ((size_t)bh * kHeadDim + d) * nbv_pad;
+    float am = 0.0f;
+    for (int b = part; b < nbv_pad; b += 2) {
+      if (b >= nbv) {
+        vb[b] = 0;
+        continue;
+      }
+      const size_t o = ((size_t)bh * nb + 2 * b) * kHeadDim + d;
+      const bool two = 2 * b + 1 < nb;
+      const double bs = ws.v_sum[o] + (two ? ws.v_sum[o + kHeadDim] : 0.0);
+      const float lo = two ? fminf(ws.v_min[o], ws.v_min[o + kHeadDim]) : ws.v_min[o];
+      const float hi = two ? fmaxf(ws.v_max[o], ws.v_max[o + kHeadDim]) : ws.v_max[o];
+      const int n = min(2 * kBlock, S - 2 * kBlock * b);
+      const uint32_t mb = bf16_bits_rne((float)(bs / (double)n));
+      const float m16 = __uint_as_float(mb << 16);
+      vb[b] = (uint16_t)mb;
+      am = fmaxf(am, fmaxf(fabsf(__fsub_rn(hi, m16)), fabsf(__fsub_rn(lo, m16))));
+    }
+    ram[part][d] = am;
+  }
   __syncthreads();
-  if (part == 0) {
+  if (part == 0 && v_bmean) {
+    float sc, inv;
+    scales_from_amax(fmaxf(ram[0][d], ram[1][d]), &sc, &inv);
+    v_scale[(size_t)bh * kHeadDim + d] = sc;
+    ws.v_inv[(size_t)bh * kHeadDim + d] = inv;
+    if (k_global) k_mean[(size_t)bh * kHeadDim + d] = (float)((rk[0][d] + rk[1][d]) / (double)S);
+  } else if (part == 0) {
     const float mean = (float)((rs[0][d] + rs[1][d]) / (double)S);
     const float lo = fminf(rmn[0][d], rmn[1][d]);
     const float hi = fmaxf(rmx[0][d], rmx[1][d]);
@@ -301,7 +350,8 @@ __global__ __launch_bounds__(kThreads) void quant_reduce_kernel(
 __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint8_t* __restrict__ K8,
     uint8_t* __restrict__ V8, float* __restrict__ k_scale, const float* __restrict__ k_mean,
-    const float* __restrict__ v_mean, Workspace ws, int S, int nb, int k_global) {
+    const float* __restrict__ v_mean, const uint16_t* __restrict__ v_bmean, int nbv_pad,
+    Workspace ws, int S, int nb, int k_global) {
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock][kHeadDim];  // [key][channel]
   const int bh = blockIdx.x / nb;
@@ -314,7 +364,9 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
   float vm[8], vi[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    vm[i] = v_mean[(size_t)bh * kHeadDim + 8 * c + i];
+    vm[i] = v_bmean ? __uint_as_float((uint32_t)v_bmean[((size_t)bh * kHeadDim + 8 * c + i) * nbv_pad +
+                                                        (blk >> 1)] << 16)
+                    : v_mean[(size_t)bh * kHeadDim + 8 * c + i];
     vi[i] = ws.v_inv[(size_t)bh * kHeadDim + 8 * c + i];
   }
 #pragma unroll
@@ -414,8 +466,8 @@ size_t quant_fp8_workspace_bytes(int B, int H, int S, int k_mean_blocks) {
 
 hipError_t launch_quant_fp8(const void* q, const void* k, const void* v, void* q8, void* k8,
                             void* v8, float* q_scale, float* k_scale, float* k_mean,
-                            int k_mean_blocks, float* v_mean, float* v_scale, void* workspace,
-                            int B, int H, int S, hipStream_t stream) {
+                            int k_mean_blocks, float* v_mean, void* v_bmean, float* v_scale,
+                            void* workspace, int B, int H, int S, hipStream_t stream) {
   const int nb = (S + kBlock - 1) / kBlock;
   const int BH = B * H;
   // With a single block the block mean is the global mean.
@@ -428,14 +480,16 @@ hipError_t launch_quant_fp8(const void* q, const void* k, const void* v, void* q
                      static_cast<uint8_t*>(k8), q_scale, k_scale, k_mean, ws, S, nb, k_global);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  uint16_t* vbm = static_cast<uint16_t*>(v_bmean);
+  const int nbv_pad = vsmooth_blocks_padded(S);
   hipLaunchKernelGGL(quant_reduce_kernel, dim3(BH), dim3(kThreads), 0, stream, v_mean, v_scale,
-                     k_mean, ws, S, nb, k_global);
+                     k_mean, vbm, nbv_pad, ws, S, nb, k_global);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(quant_residual_kernel, dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<uint8_t*>(k8), static_cast<uint8_t*>(v8), k_scale, k_mean, v_mean,
-                     ws, S, nb, k_global);
+                     vbm, nbv_pad, ws, S, nb, k_global);
   return hipGetLastError();
 }
 
