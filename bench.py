@@ -192,7 +192,7 @@ def main():
         "peak_fraction": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_kernel<false>",
+            "kernel": "attn_fwd_bf16_kernel<0>",
             "achieved": round(tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -219,6 +219,25 @@ def main():
         "tflops": round(causal_flop / (ms_c * 1e-3) / 1e12, 2),
         "peak_fraction": round(causal_flop / (ms_c * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
     }
+
+    # block-sparse variant on a seeded 25% map (each 256-query group keeps a
+    # quarter of the key tiles plus its own); FLOP over scored pairs only
+    mask = inputs.make_block_mask(w.B, w.H, w.S, 0.25, seed=w.seed)
+    rows_qb = np.minimum(128, w.S - 128 * np.arange(mask.shape[2]))
+    keys_kt = np.minimum(64, w.S - 64 * np.arange(mask.shape[3]))
+    sp_pairs = int((mask.astype(np.int64) * rows_qb[:, None] * keys_kt[None, :]).sum())
+    sparse_flop = 4 * sp_pairs * w.D
+    mask_dev = torch.from_numpy(mask).cuda()
+    log("[bench] bf16 block-sparse attention")
+    ms_s = time_launches(lambda: binding.vdit_attn_fwd_block_sparse(q, k, v, mask_dev, o=o, scale=scale),
+                         args.steps, args.warmup)
+    result["block_sparse"] = {
+        "density": round(sp_pairs / (w.B * w.H * w.S * w.S), 4),
+        "ms": round(ms_s, 4),
+        "tflops": round(sparse_flop / (ms_s * 1e-3) / 1e12, 2),
+        "peak_fraction": round(sparse_flop / (ms_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
+    del mask_dev
 
     if not args.no_fp8:
         log("[bench] fp8 pre-pass + attention")

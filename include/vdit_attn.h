@@ -169,6 +169,21 @@ vdit_status vdit_attn_fwd_fp8_expcast(const void* q8, const void* k8, const void
                                       void* stream);
 
 /*
+ * Block-sparse bf16 attention (sparse attention that skips unimportant token
+ * pairs, after the FLOPS article's "Optymalizacje", block-sparse form):
+ * query i sees key j iff block_mask[b,h,i/128,j/64] != 0.
+ *   block_mask : [B,H,ceil(S/128),ceil(S/64)] uint8 device array (any
+ *                alignment); nonzero = the 128 queries of the row block may
+ *                attend to the 64 keys of the column tile.
+ * Other arguments as vdit_attn_fwd.  Only tiles allowed for some query of a
+ * 256-query workgroup are loaded and scored.  A query row with no allowed key
+ * outputs zeros.  S > 1,048,576 is VDIT_ERR_UNSUPPORTED.
+ */
+vdit_status vdit_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
+                                       int B, int H, int S, int D, float scale,
+                                       const void* block_mask, int dtype, void* stream);
+
+/*
  * V-Smooth with the VC-Attention article's own Demean (section 02): V loses
  * the per-channel mean of every hardware block of 128 tokens (valid tokens
  * only) instead of one mean over the sequence; the residual is quantised per

@@ -150,3 +150,16 @@ def test_vsmooth_validation():
     assert st == 1 and b"null pointer: v_bmean" in lib.vdit_last_error()
     st = lib.vdit_attn_fwd_fp8_vsmooth(A, A, A, A, A, A, 4, A + 2, A, A, 1, 2, 200, 128, 0.1, 0, None)
     assert st == 1 and b"aligned: v_bmean" in lib.vdit_last_error()
+
+
+def test_block_sparse_validation():
+    lib = binding.load()
+    st = lib.vdit_attn_fwd_block_sparse(A, A * 2, A * 3, A * 4, 1, 1, 16, 128, 0.1, None, 0, None)
+    assert st == 1 and b"null pointer: block_mask" in lib.vdit_last_error()
+    # any alignment is fine for the mask; D is checked as for the dense call
+    st = lib.vdit_attn_fwd_block_sparse(A, A * 2, A * 3, A * 4, 1, 1, 16, 64, 0.1, A + 1, 0, None)
+    assert st == 2 and b"D = 128" in lib.vdit_last_error()
+    far = 1 << 40  # fake buffers far enough apart not to overlap at this size
+    st = lib.vdit_attn_fwd_block_sparse(A, A + far, A + 2 * far, A + 3 * far, 1, 1, 1048577, 128,
+                                        0.1, A + 1, 0, None)
+    assert st == 2 and b"1048576" in lib.vdit_last_error()

@@ -57,3 +57,17 @@ def test_workload_table():
             "wan2.1-14b-720p-fp8"} <= names
     for w in inputs.WORKLOADS.values():
         assert w.S == w.frames * w.tokens_per_frame and w.D == 128
+
+
+def test_block_mask_recipe():
+    m = inputs.make_block_mask(1, 2, 1000, 0.25, seed=3)
+    assert m.shape == (1, 2, 8, 16) and m.dtype == np.uint8
+    # row blocks of one 256-query group share their selection
+    assert np.array_equal(m[:, :, 0::2], m[:, :, 1::2])
+    # every row block keeps its own key tiles and at least a quarter overall
+    for qb in range(8):
+        own = slice(qb * 2, min(16, qb * 2 + 2))
+        assert np.all(m[:, :, qb, own] == 1)
+    assert np.all(m.sum(axis=3) >= 4)
+    # seeded
+    assert np.array_equal(m, inputs.make_block_mask(1, 2, 1000, 0.25, seed=3))

@@ -200,3 +200,99 @@ def test_block_causal_full_size_sampled():
         ref = oa.attention_head(q[0, h], k[0, h], v[0, h], SCALE, rows=rows,
                                 allowed=oa.block_causal_allowed(w.S, chunk))
         check_close(got_all[i], ref, f"block-causal 720p head {h}")
+
+
+# ---- block-sparse variant (query i sees key j iff mask[i // 128, j // 64]) ----
+
+def sparse_ref(q_bits, k_bits, v_bits, mask, rows=None, scale=SCALE):
+    B, H, S, _ = q_bits.shape
+    n = S if rows is None else len(rows)
+    out = np.empty((B, H, n, 128))
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = oa.attention_head(q_bits[b, h], k_bits[b, h], v_bits[b, h], scale, rows=rows,
+                                          allowed=oa.tile_mask_allowed(S, 128, 64, mask[b, h]))
+    return out
+
+
+def run_sparse(q_bits, k_bits, v_bits, mask, scale=SCALE):
+    import torch
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    o = binding.vdit_attn_fwd_block_sparse(q, k, v, torch.from_numpy(mask).cuda(), scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def random_mask(B, H, S, density, seed):
+    """Independent per 128-row block (so the two blocks of a workgroup
+    disagree); every row block keeps at least one tile."""
+    g = np.random.default_rng(seed)
+    nqb, nkt = -(-S // 128), -(-S // 64)
+    m = (g.random((B, H, nqb, nkt)) < density).astype(np.uint8)
+    m[..., g.integers(0, nkt, (B, H, nqb)).reshape(B, H, nqb, 1) == np.arange(nkt)] = 1
+    return m
+
+
+@pytest.mark.parametrize("S,density", [(1, 1.0), (65, 0.5), (300, 0.3), (1000, 0.1), (1000, 0.6),
+                                       (2049, 0.25), (3000, 0.05)])
+def test_block_sparse_sweep(S, density):
+    B, H = 1, 3
+    g = np.random.default_rng(S + int(100 * density))
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((B, H, S, 128)).astype(np.float32)) for _ in range(3)]
+    mask = random_mask(B, H, S, density, S)
+    log(f"block-sparse S={S} density={density}")
+    got = f32_of(run_sparse(*x, mask))
+    check_close(got, sparse_ref(*x, mask), f"block-sparse S={S} d={density}", ulp_slack=True)
+
+
+def test_block_sparse_full_mask_is_dense_bitwise():
+    import torch
+    g = np.random.default_rng(44)
+    S = 1500
+    x = [to_dev(inputs.f32_to_bf16_bits(g.standard_normal((2, 2, S, 128)).astype(np.float32)))
+         for _ in range(3)]
+    mask = torch.ones((2, 2, -(-S // 128), -(-S // 64)), dtype=torch.uint8, device="cuda")
+    a = binding.vdit_attn_fwd(*x, scale=SCALE)
+    b = binding.vdit_attn_fwd_block_sparse(*x, mask, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_block_sparse_empty_row_blocks_give_zeros():
+    """Row blocks with no allowed tile output zeros (a whole workgroup, and one
+    of the two blocks of a workgroup); the other rows follow the oracle."""
+    B, H, S = 1, 2, 1000
+    g = np.random.default_rng(45)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((B, H, S, 128)).astype(np.float32)) for _ in range(3)]
+    mask = random_mask(B, H, S, 0.3, 46)
+    mask[:, :, 2:4] = 0   # workgroup 1 (rows 256-511) entirely
+    mask[:, 1, 5] = 0     # second block of workgroup 2 in head 1
+    got = f32_of(run_sparse(*x, mask))
+    empty = np.zeros((B, H, S), bool)
+    empty[:, :, 256:512] = True
+    empty[:, 1, 640:768] = True
+    assert np.all(got[empty] == 0.0)
+    rows = np.flatnonzero(~empty[0, 0] & ~empty[0, 1])
+    ref = sparse_ref(*x, mask, rows=rows)
+    check_close(got[:, :, rows], ref, "block-sparse with empty blocks", ulp_slack=True)
+
+
+def test_block_sparse_full_size_sampled():
+    """720p workload with the benchmark's 25% mask, oracle rows sampled on
+    three heads (all rows of two workgroups, the ragged tail)."""
+    import torch
+    w = inputs.get_workload("wan2.1-14b-720p")
+    q, k, v = inputs.make_inputs(w)
+    mask = inputs.make_block_mask(w.B, w.H, w.S, 0.25, seed=w.seed)
+    o = run_sparse(q, k, v, mask)
+    rows = np.unique(np.concatenate([sample_rows(w.S, n_random=32), np.arange(256, 512)]))
+    heads = workload_heads(w.H)
+    got_all = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+    del o
+    torch.cuda.empty_cache()
+    for i, h in enumerate(heads):
+        ref = oa.attention_head(q[0, h], k[0, h], v[0, h], SCALE, rows=rows,
+                                allowed=oa.tile_mask_allowed(w.S, 128, 64, mask[0, h]))
+        # a quarter of the keys averages less: outlier channels reach |O| ~ 4-8,
+        # where one bf16 step (2^-5) exceeds 1e-2, so the one-step slack applies
+        check_close(got_all[i], ref, f"block-sparse 720p head {h}", ulp_slack=True)

@@ -27,6 +27,7 @@ SIGNATURES = {
     "vdit_last_error": (ctypes.c_char_p, []),
     "vdit_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "vdit_attn_fwd_block_causal": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "vdit_attn_fwd_block_sparse": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _I, _P]),
     "vdit_attn_quant_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _Z,
                                  _I, _I, _I, _I, _P]),
     "vdit_attn_quant_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
@@ -128,6 +129,34 @@ def vdit_attn_fwd_block_causal(q, k, v, chunk, o=None, scale=None, stream=None):
     check(lib.vdit_attn_fwd_block_causal(
         _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
         _dev(o, torch.bfloat16, "o"), B, H, S, D, scale, int(chunk), DTYPE_BF16, _stream(stream)))
+    return o
+
+
+SPARSE_Q_BLOCK = 128
+SPARSE_K_TILE = 64
+
+
+def vdit_attn_fwd_block_sparse(q, k, v, block_mask, o=None, scale=None, stream=None):
+    """Block-sparse attention for bf16 [B, H, S, 128]: query i sees key j iff
+    block_mask[b, h, i // 128, j // 64] != 0; block_mask is a uint8 (or
+    bool) device tensor [B, H, ceil(S/128), ceil(S/64)].  Returns o."""
+    import torch
+    B, H, S, D = _shape4(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    want = (B, H, -(-S // SPARSE_Q_BLOCK), -(-S // SPARSE_K_TILE))
+    if tuple(block_mask.shape) != want:
+        raise ValueError(f"block_mask must have shape {want}, not {tuple(block_mask.shape)}")
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    if o is None:
+        o = torch.empty_like(q)
+    scale = D ** -0.5 if scale is None else float(scale)
+    lib = load()
+    check(lib.vdit_attn_fwd_block_sparse(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(o, torch.bfloat16, "o"), B, H, S, D, scale,
+        _dev(block_mask, torch.uint8, "block_mask"), DTYPE_BF16, _stream(stream)))
     return o
 
 

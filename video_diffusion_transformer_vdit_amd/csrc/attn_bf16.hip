@@ -67,11 +67,18 @@ __device__ __forceinline__ bf16x8 read_v_operand(const char* p0, const char* p1)
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <bool kBlockCausal>
+// kMode: kDense (full attention), kCausal (block-causal by chunks of `chunk`
+// tokens) or kSparse (block-sparse: block_mask[b,h,qb,kt] != 0 lets the 128
+// queries of block qb see the 64 keys of tile kt; nqb = ceil(S / 128)).
+constexpr int kDense = 0, kCausal = 1, kSparse = 2;
+constexpr int kSparseQBlock = 128;
+constexpr int kMaxSparseTiles = 16384;  // key tiles per head (S <= 1,048,576)
+
+template <int kMode>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, int S, int n_qtiles, float c,
-    int chunk) {
+    int chunk, const uint8_t* __restrict__ block_mask, int nqb) {
   // three-deep rings of K and V tiles, one LDS object per buffer
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
@@ -97,10 +104,50 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   const bool tail = (S % kBc) != 0;
   // key limits: this lane's row, this wave's first (smallest) row, and the
   // workgroup's last valid row (the largest)
-  auto key_limit = [&](int row) { return kBlockCausal ? min(S, (row / chunk + 1) * chunk) : S; };
+  // (a run-time test on chunk, not on kMode: the dense instance compiled from
+  // the compile-time form schedules its loop worse and runs 1-4% slower)
+  auto key_limit = [&](int row) { return chunk > 0 ? min(S, (row / chunk + 1) * chunk) : S; };
   const int lim = key_limit(min(qrow, S - 1));
   const int wave_lim = key_limit(min(qt * kBr + wave * 32, S - 1));
-  const int nkt = (key_limit(min(qt * kBr + kBr - 1, S - 1)) + kBc - 1) / kBc;
+  int nkt = (key_limit(min(qt * kBr + kBr - 1, S - 1)) + kBc - 1) / kBc;
+
+  // Block-sparse: the key tiles this workgroup visits, in ascending order:
+  // the union of the tiles allowed to its two 128-query blocks, each entry
+  // kt | (query blocks allowing it) << 14.  A wave (32 rows, one query block)
+  // scores a tile its block does not allow as -inf.
+  __shared__ uint16_t lds_list[kMode == kSparse ? kMaxSparseTiles : 1];
+  __shared__ int lds_cnt[kWaves];
+  const uint32_t wbit = wave < 4 ? 1u : 2u;
+  if (kMode == kSparse) {
+    const uint8_t* m0 = block_mask + ((size_t)bh * nqb + 2 * qt) * nkt_all;
+    const bool has1 = 2 * qt + 1 < nqb;
+    int nvis = 0;
+    for (int c0 = 0; c0 < nkt_all; c0 += kThreads) {
+      const int kt = c0 + tid;
+      uint32_t f = 0;
+      if (kt < nkt_all) f = (m0[kt] ? 1u : 0u) | ((has1 && m0[nkt_all + kt]) ? 2u : 0u);
+      const unsigned long long bal = __ballot(f != 0);
+      if (lane == 0) lds_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int off = nvis;
+      for (int w = 0; w < wave; ++w) off += lds_cnt[w];
+      if (f) lds_list[off + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)(kt | (f << 14));
+      for (int w = 0; w < kWaves; ++w) nvis += lds_cnt[w];
+      __syncthreads();
+    }
+    nkt = __builtin_amdgcn_readfirstlane(nvis);
+    if (nkt == 0) {  // no allowed key for any row of this workgroup: zeros
+      if (qrow < S)
+        for (int d = 0; d < kHeadDim; d += 8)
+          *reinterpret_cast<u32x4*>(Oh + (size_t)qrow * kHeadDim + d) = u32x4{0u, 0u, 0u, 0u};
+      return;
+    }
+  }
+  // key tile of loop step t (clamped: steps past the end reload the last one)
+  auto tile_of = [&](int t) __attribute__((always_inline)) {
+    t = min(t, nkt - 1);
+    return kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(lds_list[t] & 0x3fffu)) : t;
+  };
 
   // ---- per-lane constant offsets ----
   // K and V loads: wave w, load i covers tile rows 8w + 4i + lane/16; lane
@@ -132,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
 
   const uint32_t wslice = (uint32_t)wave * (4 * kLoadsPerWave * kRowBytes);
   auto issue_k = [&](int t, const void* buf) __attribute__((always_inline)) {
-    t = min(t, nkt - 1);  // past the end: reload the last tile into a free buffer
+    t = tile_of(t);  // past the end: reload the last tile into a free buffer
     const int key0 = t * kBc;
     const char* src = Kh + (size_t)key0 * kRowBytes;
     const uint32_t dst = lds_addr(buf) + wslice;
@@ -150,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     }
   };
   auto issue_v = [&](int t, const void* buf) __attribute__((always_inline)) {
-    t = min(t, nkt - 1);
+    t = tile_of(t);
     const int key0 = t * kBc;
     const char* src = Vh + (size_t)key0 * kRowBytes;
     const uint32_t dst = lds_addr(buf) + wslice;
@@ -206,13 +253,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
         if (key >= lim) s[kb][i] = -INFINITY;
       }
   };
+  // block-sparse: step t's scores -inf where this wave's query block does not
+  // allow the tile (or t is past the list), keys past S in the ragged tile
+  auto mask_sparse = [&](int t) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    uint32_t e = 0;
+    if (t < nkt) e = lds_list[t];
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int kt = (int)(e & 0x3fffu);
+    if (((e >> 14) & wbit) == 0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = -INFINITY;
+    } else if (tail && kt == nkt_all - 1) {
+      mask_tail(kt);
+    }
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
-  float m_ref = -INFINITY;  // integer-valued log2-domain reference
+  // integer-valued log2-domain reference (finite when block-sparse, so that
+  // tiles scored entirely -inf before a row's first allowed key give 0, not NaN)
+  float m_ref = kMode == kSparse ? -1e30f : -INFINITY;
   float l4[4] = {0.f, 0.f, 0.f, 0.f};
 
   // Reference update and (rare) rescale.  In the common case only the
@@ -331,7 +397,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     // keys past S (the ragged last tile, or the tile after the last, whose
     // scores come from reloaded data and must weigh nothing)
-    if ((t + 1) * kBc + kBc > wave_lim) mask_tail(t + 1);
+    if (kMode == kSparse)
+      mask_sparse(t + 1);
+    else if ((t + 1) * kBc + kBc > wave_lim)
+      mask_tail(t + 1);
     __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
     __builtin_amdgcn_sched_barrier(0);
     barrier();
@@ -346,7 +415,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   barrier();
   qk(lds_k0);
-  if (kBc > wave_lim) mask_tail(0);
+  if (kMode == kSparse)
+    mask_sparse(0);
+  else if (kBc > wave_lim)
+    mask_tail(0);
   if (!group_a) barrier();  // group B starts one phase later
 
   // three tiles per iteration, so every ring buffer is named statically
@@ -371,7 +443,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  const float inv = 1.0f / sum_halves((l4[0] + l4[1]) + (l4[2] + l4[3]));
+  const float lsum = sum_halves((l4[0] + l4[1]) + (l4[2] + l4[3]));
+  // a row with no allowed key (block-sparse) has l = 0 and outputs zeros
+  const float inv = (kMode == kSparse && lsum == 0.f) ? 0.f : 1.0f / lsum;
   if (qrow < S) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -388,15 +462,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
-                                int B, int H, int S, float scale, int chunk, hipStream_t stream) {
+                                int B, int H, int S, float scale, int chunk,
+                                const void* block_mask, hipStream_t stream) {
   const int n_qtiles = (S + kBr - 1) / kBr;
   const long long blocks = (long long)B * H * n_qtiles;
-  auto kernel = chunk > 0 ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>;
+  const int nqb = (S + kSparseQBlock - 1) / kSparseQBlock;
+  auto kernel = block_mask  ? attn_fwd_bf16_kernel<kSparse>
+                : chunk > 0 ? attn_fwd_bf16_kernel<kCausal>
+                            : attn_fwd_bf16_kernel<kDense>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), S, n_qtiles,
-                     scale * kLog2e, chunk);
+                     scale * kLog2e, chunk, static_cast<const uint8_t*>(block_mask), nqb);
   return hipGetLastError();
 }
+
+int bf16_sparse_max_tiles() { return kMaxSparseTiles; }
 
 }  // namespace vdit

@@ -80,7 +80,8 @@ const char* vdit_status_str(int status) {
 const char* vdit_last_error(void) { return g_last_error; }
 
 static vdit_status fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, int H,
-                            int S, int D, float scale, int chunk, int dtype, void* stream) {
+                            int S, int D, float scale, int chunk, const void* block_mask,
+                            int dtype, void* stream) {
   VDIT_TRY(check_ptr(q, "q"));
   VDIT_TRY(check_ptr(k, "k"));
   VDIT_TRY(check_ptr(v, "v"));
@@ -91,20 +92,29 @@ static vdit_status fwd_bf16(const void* q, const void* k, const void* v, void* o
   const size_t bytes = (size_t)B * H * S * D * 2;
   if (overlaps(o, q, bytes, bytes) || overlaps(o, k, bytes, bytes) || overlaps(o, v, bytes, bytes))
     return fail(VDIT_ERR_INVALID_ARG, "%s", "o overlaps an input");
-  return hip_result(vdit::launch_attn_fwd_bf16(q, k, v, o, B, H, S, scale, chunk,
+  if (block_mask && (S + 63) / 64 > vdit::bf16_sparse_max_tiles())
+    return fail(VDIT_ERR_UNSUPPORTED, "%s", "block-sparse attention supports S <= 1048576");
+  return hip_result(vdit::launch_attn_fwd_bf16(q, k, v, o, B, H, S, scale, chunk, block_mask,
                                                static_cast<hipStream_t>(stream)));
 }
 
 vdit_status vdit_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
                           int S, int D, float scale, int dtype, void* stream) {
-  return fwd_bf16(q, k, v, o, B, H, S, D, scale, 0, dtype, stream);
+  return fwd_bf16(q, k, v, o, B, H, S, D, scale, 0, nullptr, dtype, stream);
 }
 
 vdit_status vdit_attn_fwd_block_causal(const void* q, const void* k, const void* v, void* o, int B,
                                        int H, int S, int D, float scale, int chunk, int dtype,
                                        void* stream) {
   if (chunk < 1) return fail(VDIT_ERR_INVALID_ARG, "%s", "chunk must be >= 1");
-  return fwd_bf16(q, k, v, o, B, H, S, D, scale, chunk, dtype, stream);
+  return fwd_bf16(q, k, v, o, B, H, S, D, scale, chunk, nullptr, dtype, stream);
+}
+
+vdit_status vdit_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, int B,
+                                       int H, int S, int D, float scale, const void* block_mask,
+                                       int dtype, void* stream) {
+  if (!block_mask) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: block_mask");
+  return fwd_bf16(q, k, v, o, B, H, S, D, scale, 0, block_mask, dtype, stream);
 }
 
 static vdit_status quant_fp8(const void* q, const void* k, const void* v, void* q8, void* k8,

@@ -6,8 +6,11 @@
 
 namespace vdit {
 
+// chunk > 0: block-causal; block_mask != nullptr: block-sparse
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
-                                int B, int H, int S, float scale, int chunk, hipStream_t stream);
+                                int B, int H, int S, float scale, int chunk,
+                                const void* block_mask, hipStream_t stream);
+int bf16_sparse_max_tiles();
 
 size_t quant_fp8_workspace_bytes(int B, int H, int S, int k_mean_blocks);
 

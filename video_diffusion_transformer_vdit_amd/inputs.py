@@ -44,6 +44,7 @@ __all__ = [
     "make_inputs",
     "outlier_channels",
     "k_offsets",
+    "make_block_mask",
 ]
 
 
@@ -159,3 +160,32 @@ def make_inputs(w: Workload | str, threads: int = 8):
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(job, jobs))
     return out["q"], out["k"], out["v"]
+
+
+def make_block_mask(B: int, H: int, S: int, density: float, seed: int,
+                    q_group: int = 256, q_block: int = 128, k_tile: int = 64) -> np.ndarray:
+    """Seeded block-sparse map, uint8 [B, H, ceil(S/q_block), ceil(S/k_tile)].
+
+    Stand-in for a learned or score-based selection (sparse attention that
+    skips unimportant token pairs): for every group of ``q_group`` queries a
+    ``density`` fraction of the key tiles is drawn uniformly at random, plus
+    the tiles holding the group's own tokens, and every ``q_block`` row block
+    of the group takes that selection.  Every row block keeps at least one
+    key tile."""
+    g = np.random.default_rng(seed)
+    nqb = -(-S // q_block)
+    nkt = -(-S // k_tile)
+    per = q_group // q_block
+    ngroups = -(-nqb // per)
+    mask = np.zeros((B, H, nqb, nkt), np.uint8)
+    n_pick = max(1, int(round(density * nkt)))
+    for b in range(B):
+        for h in range(H):
+            for gi in range(ngroups):
+                sel = np.zeros(nkt, bool)
+                sel[g.choice(nkt, n_pick, replace=False)] = True
+                lo = gi * q_group // k_tile
+                hi = min(nkt, -(-min(S, (gi + 1) * q_group) // k_tile))
+                sel[lo:hi] = True
+                mask[b, h, gi * per:(gi + 1) * per] = sel
+    return mask
