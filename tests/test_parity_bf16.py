@@ -296,3 +296,34 @@ def test_block_sparse_full_size_sampled():
         # a quarter of the keys averages less: outlier channels reach |O| ~ 4-8,
         # where one bf16 step (2^-5) exceeds 1e-2, so the one-step slack applies
         check_close(got_all[i], ref, f"block-sparse 720p head {h}", ulp_slack=True)
+
+
+# ---- size limits: the largest sequence the block-sparse list allows, many heads ----
+
+def test_max_sequence_length_sampled():
+    """S = 2^20 (one head): 64-bit offsets, 16,384 key tiles; oracle rows
+    sampled, including the first and last rows and the ragged-free tail."""
+    import torch
+    S = 1 << 20
+    g = np.random.default_rng(77)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((1, 1, S, 128)).astype(np.float32)) for _ in range(3)]
+    log(f"max length S={S}: launching")
+    o = run(*x)
+    rows = np.unique(np.concatenate([[0, 1, S // 2, S - 2, S - 1], g.integers(0, S, 27)]))
+    got = o[0, 0, rows].float().cpu().numpy().astype(np.float64)
+    del o
+    torch.cuda.empty_cache()
+    log("max length: oracle rows")
+    ref = oa.attention_head(x[0][0, 0], x[1][0, 0], x[2][0, 0], SCALE, rows=rows)
+    check_close(got, ref, f"S={S}")
+
+
+def test_many_heads_small_sequence():
+    """B = 8, H = 96, S = 77: 768 heads of one ragged workgroup each."""
+    g = np.random.default_rng(78)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((8, 96, 77, 128)).astype(np.float32)) for _ in range(3)]
+    got = f32_of(run(*x))
+    sel = [(0, 0), (3, 50), (7, 95)]
+    for b, h in sel:
+        ref = oa.attention_head(x[0][b, h], x[1][b, h], x[2][b, h], SCALE)
+        check_close(got[b, h], ref, f"B={b} H={h} of 8x96", ulp_slack=True)

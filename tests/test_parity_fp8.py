@@ -225,3 +225,22 @@ def test_expcast_workload_vs_model_and_truth():
             f"ExpCast-model floor cos={fl_cos:.6f} max_abs={fl_ma:.3e}")
         assert 1 - cos <= 1.5 * (1 - fl_cos) + 1e-5
         assert ma <= 1.5 * fl_ma + 1e-3
+
+
+def test_fp8_max_sequence_length_sampled():
+    """S = 2^20 (one head) through the GPU pre-pass and fp8 attention; sampled
+    rows against the quantisation model on the oracle's own pre-pass."""
+    import torch
+    S = 1 << 20
+    q, k, v = rand_bits((1, 1, S, 128), 91), rand_bits((1, 1, S, 128), 92, 1.0, 0.5), \
+        rand_bits((1, 1, S, 128), 93, 1.0, 1.0)
+    log(f"fp8 max length S={S}")
+    z = gpu_quant(q, k, v)
+    o = binding.vdit_attn_fwd_fp8(z, scale=SCALE)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4097, S // 2, S - 1])
+    got = o[0, 0, rows].float().cpu().numpy().astype(np.float64)
+    del o, z
+    torch.cuda.empty_cache()
+    zh = ofp8.quantize_head(q[0, 0], k[0, 0], v[0, 0])
+    check_model(got, ofp8.attention_fp8_model_head(zh, SCALE, rows=rows), f"fp8 S={S}")
