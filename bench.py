@@ -272,7 +272,16 @@ def main():
             "vsmooth_expcast_attention_ms": round(ms_vx, 4),
             "vsmooth_expcast_attention_tflops": round(w.flop / (ms_vx * 1e-3) / 1e12, 2),
         })
-        del z, zv, o8
+        log("[bench] V-Smooth Group (k-means of V, 128-token clusters on average, 4 rounds)")
+        ms_g = time_launches(lambda: binding.vdit_vsmooth_group(v), max(1, args.steps // 2), 1)
+        perm, _, _ = binding.vdit_vsmooth_group(v)
+        kp = torch.empty_like(k)
+        ms_p = time_launches(lambda: binding.vdit_permute_tokens(k, perm, out=kp), args.steps, args.warmup)
+        result["fp8"].update({
+            "vsmooth_group_ms": round(ms_g, 4),
+            "permute_tokens_ms": round(ms_p, 4),
+        })
+        del z, zv, o8, kp, perm
     del o
     torch.cuda.synchronize()
 

@@ -230,6 +230,42 @@ vdit_status vdit_attn_fwd_fp8_vsmooth(const void* q8, const void* k8, const void
                                       void* o, int B, int H, int S, int D, float scale,
                                       int expcast, void* stream);
 
+/*
+ * V-Smooth Group (VC-Attention article, section 02, Group): k-means of the
+ * value tokens of every (b,h) and the permutation that lists the tokens
+ * cluster by cluster.  Permuting K and V by it (vdit_permute_tokens) leaves
+ * non-causal attention unchanged and gathers similar values into the same
+ * 128-token blocks, so the block demean of vdit_attn_quant_fp8_vsmooth takes
+ * out more of their energy.  The article reuses a permutation for several
+ * denoising steps; so can the caller.
+ * Lloyd's algorithm, deterministic: centroid c starts as token
+ * floor(c * S / n_clusters); `rounds` times: assign every token to
+ * argmin_c |mu_c|^2 - 2 v . mu_c (v . mu on bf16 MFMAs with mu split into
+ * bf16 high and residual parts; ties to the lowest c), sort stably by
+ * cluster, mu_c = fp32 mean of the cluster's tokens (empty: unchanged); then
+ * a final assignment and sort.
+ *   v         : [B,H,S,D] bf16 (in), D = 128
+ *   perm      : [B,H,S] int32 (out): perm[i] = token placed at position i,
+ *               tokens ordered by (cluster, token index)
+ *   labels    : [B,H,S] int32 (out): cluster of every token (final assignment)
+ *   centroids : [B,H,n_clusters,D] float (out): the last centroids
+ *   1 <= n_clusters <= min(S, 4096) (ceil(S/128) gives one cluster per
+ *   hardware block on average), 0 <= rounds <= 64; workspace of at least
+ *   vdit_vsmooth_group_workspace_size() bytes, 16-byte aligned.
+ */
+size_t vdit_vsmooth_group_workspace_size(int B, int H, int S, int D, int n_clusters);
+vdit_status vdit_vsmooth_group(const void* v, int* perm, int* labels, float* centroids,
+                               int B, int H, int S, int D, int n_clusters, int rounds,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * out[b,h,i,:] = x[b,h,perm[b,h,i],:] for bf16 [B,H,S,D] rows (apply the
+ * same perm to K and V).  perm must be a permutation of 0..S-1 per (b,h)
+ * (not checked); out must not overlap x.
+ */
+vdit_status vdit_permute_tokens(const void* x, const int* perm, void* out,
+                                int B, int H, int S, int D, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -163,3 +163,18 @@ def test_block_sparse_validation():
     st = lib.vdit_attn_fwd_block_sparse(A, A + far, A + 2 * far, A + 3 * far, 1, 1, 1048577, 128,
                                         0.1, A + 1, 0, None)
     assert st == 2 and b"1048576" in lib.vdit_last_error()
+
+
+def test_vsmooth_group_validation():
+    lib = binding.load()
+    assert lib.vdit_vsmooth_group_workspace_size(1, 2, 75600, 128, 591) > 0
+    assert lib.vdit_vsmooth_group_workspace_size(1, 2, 100, 128, 101) == 0   # more clusters than tokens
+    assert lib.vdit_vsmooth_group_workspace_size(1, 2, 10 ** 6, 128, 4097) == 0
+    st = lib.vdit_vsmooth_group(A, A, A, A, 1, 2, 100, 128, 0, 4, A, 1 << 30, None)
+    assert st == 1 and b"n_clusters" in lib.vdit_last_error()
+    st = lib.vdit_vsmooth_group(A, A, A, A, 1, 2, 100, 128, 10, 65, A, 1 << 30, None)
+    assert st == 1 and b"rounds" in lib.vdit_last_error()
+    st = lib.vdit_vsmooth_group(A, A, A, A, 1, 2, 100, 128, 10, 4, A, 16, None)
+    assert st == 1 and b"workspace too small" in lib.vdit_last_error()
+    st = lib.vdit_permute_tokens(A, A, A, 1, 1, 16, 128, None)
+    assert st == 1 and b"overlaps" in lib.vdit_last_error()

@@ -38,6 +38,9 @@ SIGNATURES = {
     "vdit_attn_vsmooth_blocks": (_I, [_I]),
     "vdit_attn_fwd_fp8_vsmooth": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F,
                                        _I, _P]),
+    "vdit_vsmooth_group_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "vdit_vsmooth_group": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]),
+    "vdit_permute_tokens": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
 }
 
 _lib = None
@@ -258,3 +261,39 @@ def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False):
         kmb, _dev(z["v_mean"], torch.float32, "v_mean"), _dev(z["v_scale"], torch.float32, "v_scale"),
         _dev(o, torch.bfloat16, "o"), B, H, S, D, scale, _stream(stream)))
     return o
+
+
+def vdit_vsmooth_group(v, n_clusters=None, rounds=4, stream=None):
+    """k-means grouping of the value tokens of bf16 v [B, H, S, 128]; returns
+    (perm, labels, centroids): int32 [B, H, S], int32 [B, H, S] and float32
+    [B, H, n_clusters, 128].  n_clusters defaults to ceil(S / 128)."""
+    import torch
+    B, H, S, D = _shape4(v)
+    k = -(-S // 128) if n_clusters is None else int(n_clusters)
+    lib = load()
+    ws_bytes = int(lib.vdit_vsmooth_group_workspace_size(B, H, S, D, k))
+    if ws_bytes == 0:
+        raise ValueError("invalid shape or n_clusters for V-Smooth Group")
+    perm = torch.empty((B, H, S), dtype=torch.int32, device=v.device)
+    labels = torch.empty((B, H, S), dtype=torch.int32, device=v.device)
+    cent = torch.empty((B, H, k, D), dtype=torch.float32, device=v.device)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=v.device)
+    check(lib.vdit_vsmooth_group(
+        _dev(v, torch.bfloat16, "v"), _dev(perm, torch.int32, "perm"),
+        _dev(labels, torch.int32, "labels"), _dev(cent, torch.float32, "centroids"),
+        B, H, S, D, k, int(rounds), _dev(ws, torch.uint8, "workspace"), ws_bytes, _stream(stream)))
+    return perm, labels, cent
+
+
+def vdit_permute_tokens(x, perm, out=None, stream=None):
+    """out[b, h, i] = x[b, h, perm[b, h, i]] for bf16 [B, H, S, 128]."""
+    import torch
+    B, H, S, D = _shape4(x)
+    if tuple(perm.shape) != (B, H, S):
+        raise ValueError("perm must have shape [B, H, S]")
+    if out is None:
+        out = torch.empty_like(x)
+    lib = load()
+    check(lib.vdit_permute_tokens(_dev(x, torch.bfloat16, "x"), _dev(perm, torch.int32, "perm"),
+                                  _dev(out, torch.bfloat16, "out"), B, H, S, D, _stream(stream)))
+    return out

@@ -237,4 +237,42 @@ vdit_status vdit_attn_fwd_fp8_vsmooth(const void* q8, const void* k8, const void
                  B, H, S, D, scale, expcast == 1, stream);
 }
 
+static bool group_args_ok(int S, int n_clusters, int rounds) {
+  return n_clusters >= 1 && n_clusters <= vdit::kGroupMaxClusters && n_clusters <= S &&
+         rounds >= 0 && rounds <= 64;
+}
+
+size_t vdit_vsmooth_group_workspace_size(int B, int H, int S, int D, int n_clusters) {
+  if (check_shape(B, H, S, D) != VDIT_OK || !group_args_ok(S, n_clusters, 0)) return 0;
+  return vdit::group_workspace_bytes(B, H, S, n_clusters);
+}
+
+vdit_status vdit_vsmooth_group(const void* v, int* perm, int* labels, float* centroids, int B,
+                               int H, int S, int D, int n_clusters, int rounds, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  VDIT_TRY(check_ptr(v, "v"));
+  VDIT_TRY(check_ptr(perm, "perm"));
+  VDIT_TRY(check_ptr(labels, "labels"));
+  VDIT_TRY(check_fptr(centroids, "centroids"));
+  VDIT_TRY(check_ptr(workspace, "workspace"));
+  VDIT_TRY(check_shape(B, H, S, D));
+  if (!group_args_ok(S, n_clusters, rounds))
+    return fail(VDIT_ERR_INVALID_ARG, "%s", "need 1 <= n_clusters <= min(S, 4096), 0 <= rounds <= 64");
+  if (workspace_bytes < vdit::group_workspace_bytes(B, H, S, n_clusters))
+    return fail(VDIT_ERR_INVALID_ARG, "%s", "workspace too small");
+  return hip_result(vdit::launch_vsmooth_group(v, perm, labels, centroids, workspace, B, H, S,
+                                               n_clusters, rounds, static_cast<hipStream_t>(stream)));
+}
+
+vdit_status vdit_permute_tokens(const void* x, const int* perm, void* out, int B, int H, int S,
+                                int D, void* stream) {
+  VDIT_TRY(check_ptr(x, "x"));
+  VDIT_TRY(check_ptr(perm, "perm"));
+  VDIT_TRY(check_ptr(out, "out"));
+  VDIT_TRY(check_shape(B, H, S, D));
+  const size_t bytes = (size_t)B * H * S * D * 2;
+  if (overlaps(out, x, bytes, bytes)) return fail(VDIT_ERR_INVALID_ARG, "%s", "out overlaps x");
+  return hip_result(vdit::launch_permute_rows(x, perm, out, B, H, S, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -35,4 +35,13 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                const float* v_scale, void* o, int B, int H, int S, float scale,
                                bool expcast, hipStream_t stream);
 
+// V-Smooth Group: k-means of V tokens and the stable cluster permutation
+constexpr int kGroupMaxClusters = 4096;
+size_t group_workspace_bytes(int B, int H, int S, int k);
+hipError_t launch_vsmooth_group(const void* v, int* perm, int* labels, float* centroids,
+                                void* workspace, int B, int H, int S, int k, int rounds,
+                                hipStream_t stream);
+hipError_t launch_permute_rows(const void* x, const int* perm, void* out, int B, int H, int S,
+                               hipStream_t stream);
+
 }  // namespace vdit
