@@ -21,18 +21,19 @@ Sources on the pages
   per-row total variation stays under 3.64% plus underflow tails
   [VC-Attention article, §03].
 
-Readings taken where the pages are silent (each also listed in the design
-notes): Q and K use one scale per 64-token block; K is smoothed by the mean
-of each 64-token block (or one global mean per head), and the per-block mean
-is compensated exactly by adding q_hat . k_mean_b to the scores of block b;
-V is smoothed by one per-channel mean over the sequence with one per-channel
-scale, or (the article's Demean, ``v_mean="block"``) by the per-channel mean
-of each 128-token block (valid tokens only) rounded to bf16 (the 16-bit
-mean), with one per-channel scale of the residual over the sequence; P is quantised as E4M3(448 * 2^(t - M)) where t is the log2-domain
-score and M the integer ceiling of the row maximum of t; the row sum is the
-sum of the quantised weights (so the weights of a row sum to one and the
-mean restore is exact); ExpCast rounds 8 (t - M) + 8 log2(448) + 55.65 to
-the nearest integer, ties to even, clamped to [0, 255].
+Readings taken where the pages are silent: Q and K use one scale per
+64-token block; K is smoothed by the mean of each 64-token block (or one
+global mean per head), and the per-block mean is compensated exactly by
+adding q_hat . k_mean_b to the scores of block b; V is smoothed by one per-
+channel mean over the sequence with one per-channel scale, or (the article's
+Demean, ``v_mean="block"``) by the per-channel mean of each 128-token block
+(valid tokens only) rounded to bf16 (the 16-bit mean), with one per-channel
+scale of the residual over the sequence; P is quantised as E4M3(448 * 2^(t -
+M)) where t is the log2-domain score and M the integer ceiling of the row
+maximum of t; the row sum is the sum of the quantised weights (so the
+weights of a row sum to one and the mean restore is exact); ExpCast rounds 8
+(t - M) + 8 log2(448) + 55.65 to the nearest integer, ties to even, clamped
+to [0, 255].
 
 Precision of the integer-valued decisions (codes): the pre-pass takes them
 in the precision the kernel takes them in, so the codes can be compared bit

@@ -10,19 +10,17 @@ on the first quarter of the denoising steps and a permutation is reused for
 four neighbouring steps; after sorting, subtracting the mean of each 128-token
 block removes far more of the block's energy (36%) than in sequence order (8%).
 
-Readings taken where the article is silent (each also listed in the design
-notes): Lloyd's k-means with a fixed number of rounds on the 128 channels of
-each V token (the article names only "online k-means"); ``n_clusters``
-defaults to ceil(S / 128), one cluster per hardware block on average;
-deterministic start: centroid c is token floor(c * S / n_clusters);
-assignment: argmin over c of |mu_c|^2 - 2 v . mu_c (the token's own norm is
-the same for every c), ties to the lowest c; update: the mean of the
-assigned tokens, an empty cluster keeps its centroid; after the last update
-one more assignment; the permutation lists the tokens by (cluster, token
-index), i.e. a stable sort by cluster.  "Energy removed" by block means is
-sum_b n_b |mean_b|^2 / sum_j |v_j|^2 (what subtracting each block's mean
-takes out of the sum of squares).
-"""
+Readings taken where the article is silent: Lloyd's k-means with a fixed
+number of rounds on the 128 channels of each V token (the article names only
+"online k-means"); ``n_clusters`` defaults to ceil(S / 128), one cluster per
+hardware block on average; deterministic start: centroid c is token floor(c
+* S / n_clusters); assignment: argmin over c of |mu_c|^2 - 2 v . mu_c (the
+token's own norm is the same for every c), ties to the lowest c; update: the
+mean of the assigned tokens, an empty cluster keeps its centroid; after the
+last update one more assignment; the permutation lists the tokens by
+(cluster, token index), i.e. a stable sort by cluster. "Energy removed" by
+block means is sum_b n_b |mean_b|^2 / sum_j |v_j|^2 (what subtracting each
+block's mean takes out of the sum of squares). """
 
 from __future__ import annotations
 
