@@ -241,7 +241,8 @@ def expcast_byte(log2_v) -> np.ndarray:
 def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
                              p_quant: bool = True, p_scale: float = E4M3_MAX,
                              chunk: int = 256, p_cast: str = "exp",
-                             reference: str | None = None, v_block: int = 128) -> np.ndarray:
+                             reference: str | None = None, v_block: int = 128,
+                             allowed=None) -> np.ndarray:
     """Quantisation model of the fp8 attention for one head, in fp64.
 
     Steps: dequantise Q_hat = dec(q8) q_scale, K_hat = dec(k8) k_scale,
@@ -251,6 +252,9 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
     with p_cast="expcast" the E4M3 byte is the ExpCast byte of p_scale p,
     expcast_byte(t - M + log2(p_scale)));
     l_i = sum_j w_ij;  O_i = (sum_j w_ij V_hat_j) / l_i + v_mean.
+    ``allowed(rows) -> bool [len(rows), S]`` restricts each row to its allowed
+    keys (block-causal or block-sparse masks): the others score -inf and
+    weigh 0, and M is the maximum over the allowed keys.
     With block means (``v_bmean`` in qz, V-Smooth Demean) the mean is
     restored per key instead: O_i = sum_j w_ij (V_hat_j + v_bmean_b(j)) / l_i,
     b(j) = j // v_block (the row sum of each block's weights times its mean).
@@ -291,14 +295,18 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
         reference = "running" if p_cast == "expcast" else "final"
 
     def weights(t, M):
+        # masked scores (-inf) weigh 0, also before any allowed key is seen
+        d = np.where(np.isneginf(t), -np.inf, t - M)
         if p_cast == "expcast":
-            return e4m3_decode(expcast_byte(t - M + math.log2(p_scale))) / p_scale
-        p = np.exp2(t - M)
+            return e4m3_decode(expcast_byte(d + math.log2(p_scale))) / p_scale
+        p = np.exp2(d)
         return e4m3_decode(e4m3_encode(p * p_scale)) / p_scale if p_quant else p
 
     for r0 in range(0, rows.size, chunk):
         rr = rows[r0:r0 + chunk]
         t = (qh[rr] @ keff.T) * (float(np.float64(scale)) * log2e)
+        if allowed is not None:
+            t = np.where(allowed(rr), t, -np.inf)
         if reference == "running":
             M = np.full((rr.size, 1), -np.inf)
             acc = np.zeros((rr.size, D))

@@ -423,3 +423,43 @@ def test_expcast_running_equals_final_when_the_maximum_comes_first():
     run = fp8.attention_fp8_model_head(z, scale, p_cast="expcast", reference="running")
     fin = fp8.attention_fp8_model_head(z, scale, p_cast="expcast", reference="final")
     np.testing.assert_allclose(run, fin, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask", ["causal", "sparse"])
+def test_masked_model_without_p_quantisation_is_masked_attention(mask):
+    """With P unquantised, the masked model is the masked definition on the
+    dequantised operands; with quantisation every weight of a masked key is 0
+    (exp and ExpCast, final and running references)."""
+    g = np.random.default_rng(11)
+    S, D = 300, 128
+    nb = -(-S // 64)
+    z = _random_qz(S, D, 12, nb)
+    if mask == "causal":
+        allowed = oa.block_causal_allowed(S, 70)
+    else:
+        m = g.random((-(-S // 128), nb)) < 0.4
+        m[:, 0] = True
+        allowed = oa.tile_mask_allowed(S, 128, 64, m)
+    blk = np.arange(S) // 64
+    qh = fp8.e4m3_decode(z["q8"]) * z["q_scale"][blk][:, None].astype(np.float64)
+    kh = fp8.e4m3_decode(z["k8"]) * z["k_scale"][blk][:, None].astype(np.float64) + z["k_mean"][blk]
+    vh = fp8.e4m3_decode(z["v8"]) * z["v_scale"][None, :].astype(np.float64) + z["v_mean"]
+    scale = 0.07
+    ref = oa.attention_head(qh, kh, vh, scale, allowed=allowed)
+    got = fp8.attention_fp8_model_head(z, scale, p_quant=False, allowed=allowed)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+    # quantised weights: permuting the values of the keys row 0 may not see
+    # changes nothing in row 0
+    hidden = np.flatnonzero(~allowed(np.arange(1))[0])
+    assert hidden.size > 10
+    z2 = dict(z)
+    v2 = z["v8"].copy()
+    v2[hidden] = v2[hidden[::-1]]
+    z2["v8"] = v2
+    for p_cast in ("exp", "expcast"):
+        for reference in ("final", "running"):
+            kw = dict(p_cast=p_cast, reference=reference, allowed=allowed)
+            a = fp8.attention_fp8_model_head(z, scale, **kw)
+            b = fp8.attention_fp8_model_head(z2, scale, **kw)
+            assert np.all(np.isfinite(a))
+            np.testing.assert_array_equal(a[0], b[0])
