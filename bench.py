@@ -237,7 +237,6 @@ def main():
         "tflops": round(sparse_flop / (ms_s * 1e-3) / 1e12, 2),
         "peak_fraction": round(sparse_flop / (ms_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
     }
-    del mask_dev
 
     if not args.no_fp8:
         log("[bench] fp8 pre-pass + attention")
@@ -259,6 +258,19 @@ def main():
             "expcast_attention_tflops": round(w.flop / (ms_x * 1e-3) / 1e12, 2),
             "expcast_attention_peak_fraction": round(w.flop / (ms_x * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
         }
+        log("[bench] fp8 block-causal and block-sparse attention (same chunk and map as bf16)")
+        for name, kw, flop in (("block_causal", {"chunk": chunk}, causal_flop),
+                               ("block_sparse", {"block_mask": mask_dev}, sparse_flop)):
+            ms_m = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o8, **kw),
+                                 args.steps, args.warmup)
+            ms_mx = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o8, expcast=True, **kw),
+                                  args.steps, args.warmup)
+            result["fp8"].update({
+                f"{name}_attention_ms": round(ms_m, 4),
+                f"{name}_attention_tflops": round(flop / (ms_m * 1e-3) / 1e12, 2),
+                f"{name}_expcast_attention_ms": round(ms_mx, 4),
+                f"{name}_expcast_attention_tflops": round(flop / (ms_mx * 1e-3) / 1e12, 2),
+            })
         log("[bench] fp8 with V-Smooth block means (128-token blocks)")
         zv = binding.vdit_attn_quant_fp8(q, k, v, v_mean="block")
         ms_vq = time_launches(lambda: binding.vdit_attn_quant_fp8(q, k, v, out=zv), args.steps, args.warmup)
@@ -282,7 +294,7 @@ def main():
             "permute_tokens_ms": round(ms_p, 4),
         })
         del z, zv, o8, kp, perm
-    del o
+    del o, mask_dev
     torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:

@@ -184,6 +184,26 @@ vdit_status vdit_attn_fwd_block_sparse(const void* q, const void* k, const void*
                                        const void* block_mask, int dtype, void* stream);
 
 /*
+ * fp8 attention with a key mask, on the outputs of vdit_attn_quant_fp8
+ * (per-channel V mean).  Scores, weights (expcast = 1: ExpCast bytes,
+ * 0: exp2 then E4M3) and restore as vdit_attn_fwd_fp8, restricted to the
+ * allowed keys of each query:
+ *   chunk > 0        block-causal as vdit_attn_fwd_block_causal;
+ *   block_mask != 0  block-sparse as vdit_attn_fwd_block_sparse (uint8
+ *                    [B,H,ceil(S/128),ceil(S/64)], S <= 1,048,576);
+ *   neither          full attention (vdit_attn_fwd_fp8).
+ * Giving both is VDIT_ERR_INVALID_ARG; so is chunk < 0.  A query row with no
+ * allowed key outputs zeros.
+ */
+vdit_status vdit_attn_fwd_fp8_masked(const void* q8, const void* k8, const void* v8,
+                                     const float* q_scale, const float* k_scale,
+                                     const float* k_mean, int k_mean_blocks,
+                                     const float* v_mean, const float* v_scale,
+                                     void* o, int B, int H, int S, int D, float scale,
+                                     int chunk, const void* block_mask, int expcast,
+                                     void* stream);
+
+/*
  * V-Smooth with the VC-Attention article's own Demean (section 02): V loses
  * the per-channel mean of every hardware block of 128 tokens (valid tokens
  * only) instead of one mean over the sequence; the residual is quantised per

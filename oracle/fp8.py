@@ -302,31 +302,33 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
         p = np.exp2(d)
         return e4m3_decode(e4m3_encode(p * p_scale)) / p_scale if p_quant else p
 
-    for r0 in range(0, rows.size, chunk):
-        rr = rows[r0:r0 + chunk]
-        t = (qh[rr] @ keff.T) * (float(np.float64(scale)) * log2e)
-        if allowed is not None:
-            t = np.where(allowed(rr), t, -np.inf)
-        if reference == "running":
-            M = np.full((rr.size, 1), -np.inf)
-            acc = np.zeros((rr.size, D))
-            l = np.zeros((rr.size, 1))
-            for j0 in range(0, S, block):
-                tt = t[:, j0:j0 + block]
-                Mn = np.maximum(M, np.ceil(tt.max(axis=1, keepdims=True)))
-                f = np.where(np.isfinite(M), np.exp2(M - Mn), 0.0)
-                acc *= f
-                l *= f
-                M = Mn
-                w = weights(tt, M)
-                acc += w @ vh[j0:j0 + block]
-                l += w.sum(axis=1, keepdims=True)
-            out[r0:r0 + chunk] = acc / l + vm_add
-            continue
-        M = np.ceil(t.max(axis=1, keepdims=True))
-        w = weights(t, M)
-        l = w.sum(axis=1, keepdims=True)
-        out[r0:r0 + chunk] = (w @ vh) / l + vm_add
+    # -inf - -inf (a masked key before any allowed one) is discarded by np.where
+    with np.errstate(invalid="ignore"):
+        for r0 in range(0, rows.size, chunk):
+            rr = rows[r0:r0 + chunk]
+            t = (qh[rr] @ keff.T) * (float(np.float64(scale)) * log2e)
+            if allowed is not None:
+                t = np.where(allowed(rr), t, -np.inf)
+            if reference == "running":
+                M = np.full((rr.size, 1), -np.inf)
+                acc = np.zeros((rr.size, D))
+                l = np.zeros((rr.size, 1))
+                for j0 in range(0, S, block):
+                    tt = t[:, j0:j0 + block]
+                    Mn = np.maximum(M, np.ceil(tt.max(axis=1, keepdims=True)))
+                    f = np.where(np.isfinite(M), np.exp2(M - Mn), 0.0)
+                    acc *= f
+                    l *= f
+                    M = Mn
+                    w = weights(tt, M)
+                    acc += w @ vh[j0:j0 + block]
+                    l += w.sum(axis=1, keepdims=True)
+                out[r0:r0 + chunk] = acc / l + vm_add
+                continue
+            M = np.ceil(t.max(axis=1, keepdims=True))
+            w = weights(t, M)
+            l = w.sum(axis=1, keepdims=True)
+            out[r0:r0 + chunk] = (w @ vh) / l + vm_add
     return out
 
 

@@ -178,3 +178,14 @@ def test_vsmooth_group_validation():
     assert st == 1 and b"workspace too small" in lib.vdit_last_error()
     st = lib.vdit_permute_tokens(A, A, A, 1, 1, 16, 128, None)
     assert st == 1 and b"overlaps" in lib.vdit_last_error()
+
+
+def test_fp8_masked_validation():
+    lib = binding.load()
+    args = (A, A, A, A, A, A, 4, A, A, A, 1, 2, 200, 128, 0.1)
+    st = lib.vdit_attn_fwd_fp8_masked(*args, -1, None, 0, None)
+    assert st == 1 and b"chunk" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_masked(*args, 64, A + 1, 0, None)
+    assert st == 1 and b"not both" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_masked(*args, 0, None, 3, None)
+    assert st == 1 and b"expcast" in lib.vdit_last_error()

@@ -244,3 +244,138 @@ def test_fp8_max_sequence_length_sampled():
     torch.cuda.empty_cache()
     zh = ofp8.quantize_head(q[0, 0], k[0, 0], v[0, 0])
     check_model(got, ofp8.attention_fp8_model_head(zh, SCALE, rows=rows), f"fp8 S={S}")
+
+
+# ---- key masks (block-causal chunks, block-sparse tile maps) on the fp8 path ----
+
+def masked_inputs(S, seed, B=1, H=2):
+    return (rand_bits((B, H, S, 128), seed), rand_bits((B, H, S, 128), seed + 10, 1.0, 0.5),
+            rand_bits((B, H, S, 128), seed + 20, 1.0, 1.0))
+
+
+def random_tile_mask(B, H, S, density, seed):
+    """Independent per 128-row block; every row block keeps one tile or more."""
+    g = np.random.default_rng(seed)
+    nqb, nkt = -(-S // 128), -(-S // 64)
+    m = (g.random((B, H, nqb, nkt)) < density).astype(np.uint8)
+    m[..., g.integers(0, nkt, (B, H, nqb)).reshape(B, H, nqb, 1) == np.arange(nkt)] = 1
+    return m
+
+
+def masked_model(zo, allowed_of, p_cast, rows=None):
+    B, H = zo["q8"].shape[:2]
+    n = zo["q8"].shape[2] if rows is None else len(rows)
+    out = np.empty((B, H, n, 128))
+    for b in range(B):
+        for h in range(H):
+            zh = {key: val[b, h] for key, val in zo.items()}
+            out[b, h] = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows, p_cast=p_cast,
+                                                      allowed=allowed_of(b, h))
+    return out
+
+
+@pytest.mark.parametrize("p_cast", ["exp", "expcast"])
+@pytest.mark.parametrize("S,chunk", [(1, 64), (200, 64), (1000, 256), (1000, 300), (777, 100)])
+def test_fp8_block_causal_vs_quant_model(S, chunk, p_cast):
+    import torch
+    q, k, v = masked_inputs(S, 41 + S % 13)
+    zo = ofp8.quantize(q, k, v, k_mean="block")
+    log(f"fp8 block-causal S={S} chunk={chunk} {p_cast}")
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE, expcast=p_cast == "expcast", chunk=chunk)
+    torch.cuda.synchronize()
+    ref = masked_model(zo, lambda b, h: oa.block_causal_allowed(S, chunk), p_cast)
+    check_model(f32_of(o), ref, f"fp8 block-causal S={S} chunk={chunk} {p_cast}")
+
+
+def test_fp8_block_causal_with_chunk_past_s_is_dense_bitwise():
+    import torch
+    q, k, v = masked_inputs(700, 51)
+    z = zdev(ofp8.quantize(q, k, v, k_mean="block"))
+    for ec in (False, True):
+        a = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec)
+        b = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec, chunk=700)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"expcast={ec}"
+
+
+@pytest.mark.parametrize("p_cast", ["exp", "expcast"])
+@pytest.mark.parametrize("S,density", [(1, 1.0), (130, 0.5), (1000, 0.3), (1000, 0.05), (641, 0.6)])
+def test_fp8_block_sparse_vs_quant_model(S, density, p_cast):
+    import torch
+    q, k, v = masked_inputs(S, 61 + S % 7)
+    zo = ofp8.quantize(q, k, v, k_mean="block")
+    mask = random_tile_mask(1, 2, S, density, seed=S)
+    log(f"fp8 block-sparse S={S} density={density} {p_cast}")
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE, expcast=p_cast == "expcast",
+                                  block_mask=torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    ref = masked_model(zo, lambda b, h: oa.tile_mask_allowed(S, 128, 64, mask[b, h]), p_cast)
+    check_model(f32_of(o), ref, f"fp8 block-sparse S={S} d={density} {p_cast}")
+
+
+def test_fp8_block_sparse_full_mask_is_dense_bitwise():
+    import torch
+    S = 900
+    q, k, v = masked_inputs(S, 71)
+    z = zdev(ofp8.quantize(q, k, v, k_mean="block"))
+    mask = torch.ones((1, 2, -(-S // 128), -(-S // 64)), dtype=torch.uint8, device="cuda")
+    for ec in (False, True):
+        a = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec)
+        b = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec, block_mask=mask)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"expcast={ec}"
+
+
+@pytest.mark.parametrize("p_cast", ["exp", "expcast"])
+def test_fp8_block_sparse_empty_row_blocks_give_zeros(p_cast):
+    import torch
+    S = 700
+    q, k, v = masked_inputs(S, 81)
+    zo = ofp8.quantize(q, k, v, k_mean="block")
+    mask = random_tile_mask(1, 2, S, 0.4, seed=5)
+    mask[0, 0, 1] = 0          # rows 128..255 of head 0 see nothing
+    mask[0, 1, 5] = 0          # the ragged last block of head 1
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE, expcast=p_cast == "expcast",
+                                  block_mask=torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    got = f32_of(o)
+    assert np.all(got[0, 0, 128:256] == 0) and np.all(got[0, 1, 640:] == 0)
+    rows = np.r_[0:128, 256:640]
+    ref = masked_model(zo, lambda b, h: oa.tile_mask_allowed(S, 128, 64, mask[b, h]), p_cast,
+                       rows=rows)
+    check_model(got[:, :, rows], ref, f"fp8 block-sparse empty blocks {p_cast}")
+
+
+def test_fp8_masks_full_size_sampled():
+    """The 720p workload (1x40x75600x128) through the GPU pre-pass, block-causal
+    by latent frames (3600 tokens a chunk) and under a 25% tile map; sampled
+    rows of two heads against the quantisation model."""
+    import torch
+    w = inputs.get_workload("wan2.1-14b-720p-fp8")
+    q, k, v = inputs.make_inputs(w)
+    z = gpu_quant(q, k, v)
+    chunk = w.tokens_per_frame
+    mask = inputs.make_block_mask(w.B, w.H, w.S, 0.25, seed=w.seed)
+    rows = sample_rows(w.S, n_random=24)
+    heads = workload_heads(w.H)[:2]
+    outs = {}
+    for ec in (False, True):
+        log(f"fp8 720p block-causal chunk={chunk} expcast={ec}")
+        o = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec, chunk=chunk)
+        torch.cuda.synchronize()
+        outs[("causal", ec)] = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+        log(f"fp8 720p block-sparse 25% expcast={ec}")
+        o = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec,
+                                      block_mask=torch.from_numpy(mask).cuda())
+        torch.cuda.synchronize()
+        outs[("sparse", ec)] = o[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+        del o
+    del z
+    for i, h in enumerate(heads):
+        zh = ofp8.quantize_head(q[0, h], k[0, h], v[0, h])
+        for (kind, ec), got in outs.items():
+            allowed = (oa.block_causal_allowed(w.S, chunk) if kind == "causal"
+                       else oa.tile_mask_allowed(w.S, 128, 64, mask[0, h]))
+            ref = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows, allowed=allowed,
+                                                p_cast="expcast" if ec else "exp")
+            check_model(got[i], ref, f"fp8 720p {kind} expcast={ec} head {h}")

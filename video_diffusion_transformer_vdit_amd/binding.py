@@ -38,6 +38,8 @@ SIGNATURES = {
     "vdit_attn_vsmooth_blocks": (_I, [_I]),
     "vdit_attn_fwd_fp8_vsmooth": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F,
                                        _I, _P]),
+    "vdit_attn_fwd_fp8_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F,
+                                      _I, _P, _I, _P]),
     "vdit_vsmooth_group_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "vdit_vsmooth_group": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]),
     "vdit_permute_tokens": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
@@ -232,11 +234,13 @@ def vdit_attn_quant_fp8(q, k, v, k_mean_blocks=None, out=None, stream=None, v_me
     return z
 
 
-def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False):
+def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False, chunk=0, block_mask=None):
     """fp8 attention on pre-pass outputs ``z`` (dict as from vdit_attn_quant_fp8);
     returns bf16 o [B, H, S, 128].  ``expcast`` selects the ExpCast-FP8 entry
     point (P bytes written directly from the log domain).  A ``z`` holding
-    v_bmean (V block means) goes to vdit_attn_fwd_fp8_vsmooth."""
+    v_bmean (V block means) goes to vdit_attn_fwd_fp8_vsmooth; ``chunk`` > 0
+    (block-causal) or ``block_mask`` (block-sparse, uint8 [B, H, ceil(S/128),
+    ceil(S/64)]) go to vdit_attn_fwd_fp8_masked."""
     import torch
     B, H, S, D = _shape4(z["q8"])
     if o is None:
@@ -244,6 +248,24 @@ def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False):
     scale = D ** -0.5 if scale is None else float(scale)
     kmb = int(z["k_mean"].shape[2])
     lib = load()
+    if chunk or block_mask is not None:
+        if "v_bmean" in z:
+            raise ValueError("key masks take the per-channel V mean pre-pass (v_mean)")
+        if block_mask is not None:
+            want = (B, H, -(-S // 128), -(-S // 64))
+            if tuple(block_mask.shape) != want:
+                raise ValueError(f"block_mask must have shape {want}")
+            if block_mask.dtype == torch.bool:
+                block_mask = block_mask.view(torch.uint8)
+        mask_ptr = _dev(block_mask, torch.uint8, "block_mask") if block_mask is not None else None
+        check(lib.vdit_attn_fwd_fp8_masked(
+            _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),
+            _dev(z["v8"], torch.uint8, "v8"), _dev(z["q_scale"], torch.float32, "q_scale"),
+            _dev(z["k_scale"], torch.float32, "k_scale"), _dev(z["k_mean"], torch.float32, "k_mean"),
+            kmb, _dev(z["v_mean"], torch.float32, "v_mean"), _dev(z["v_scale"], torch.float32, "v_scale"),
+            _dev(o, torch.bfloat16, "o"), B, H, S, D, scale, int(chunk), mask_ptr,
+            1 if expcast else 0, _stream(stream)))
+        return o
     if "v_bmean" in z:
         check(lib.vdit_attn_fwd_fp8_vsmooth(
             _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),

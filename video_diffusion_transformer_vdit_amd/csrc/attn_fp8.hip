@@ -84,17 +84,24 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
+// Key masks (as in the bf16 kernel): kDense, kCausal (query i sees key j iff
+// j / chunk <= i / chunk) or kSparse (block_mask[b,h,i/128,j/64] != 0).
+constexpr int kDense = 0, kCausal = 1, kSparse = 2;
+constexpr int kMaxSparseTiles = 16384;
+
 // kBlockMean: one K mean per 64-token block (else one mean per head);
 // kExpCast: P8 bytes written directly from the log domain (else exp2, then
 // an E4M3 conversion); kVBlock: V means per 128-token block (v_bmean, bf16,
-// [bh][channel][nbv_pad]) restored in the loop (else one v_mean per channel)
-template <bool kBlockMean, bool kExpCast, bool kVBlock>
+// [bh][channel][nbv_pad]) restored in the loop (else one v_mean per channel;
+// kVBlock is only built for kDense); kMode: the key mask.
+template <bool kBlockMean, bool kExpCast, bool kVBlock, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const float* __restrict__ k_mean, const float* __restrict__ v_mean,
     const uint16_t* __restrict__ v_bmean, int nbv_pad, const float* __restrict__ v_scale,
-    uint16_t* __restrict__ O, int S, int n_qtiles, float c) {
+    uint16_t* __restrict__ O, int S, int n_qtiles, float c, int chunk,
+    const uint8_t* __restrict__ block_mask, int nqb) {
   // three-deep rings of K and V tiles, one LDS object per buffer
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
@@ -108,14 +115,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
-  const int qt = tile - bh * n_qtiles;
+  // block-causal: heaviest query tiles first
+  const int qt = kMode == kCausal ? n_qtiles - 1 - (tile - bh * n_qtiles) : tile - bh * n_qtiles;
   const size_t base = (size_t)bh * S * kHeadDim;
-  const int nkt = (S + kBc - 1) / kBc;
+  const int nkt_all = (S + kBc - 1) / kBc;
   const uint8_t* Q8h = Q8 + base;
   const char* K8h = reinterpret_cast<const char*>(K8 + base);
-  // V codes: nkt tiles of 8 KB per head
-  const char* V8h = reinterpret_cast<const char*>(V8) + (size_t)bh * nkt * kTileBytes;
-  const float* ksh = k_scale + (size_t)bh * nkt;
+  // V codes: nkt_all tiles of 8 KB per head
+  const char* V8h = reinterpret_cast<const char*>(V8) + (size_t)bh * nkt_all * kTileBytes;
+  const float* ksh = k_scale + (size_t)bh * nkt_all;
   uint16_t* Oh = O + base;
 
   const int tid = threadIdx.x;
@@ -125,6 +133,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const bool qok = qrow < S;
   const bool tail = (S % kBc) != 0;
 
+  // ---- key masks: the tiles this workgroup visits (nkt loop steps) ----
+  auto key_limit = [&](int row) { return kMode == kCausal ? min(S, (row / chunk + 1) * chunk) : S; };
+  const int lim = key_limit(min(qrow, S - 1));
+  const int wave_lim = key_limit(min(qt * kBr + wave * 32, S - 1));
+  int nkt = (key_limit(min(qt * kBr + kBr - 1, S - 1)) + kBc - 1) / kBc;
+  // block-sparse: the union of the tiles allowed to the workgroup's two
+  // 128-query blocks, ascending, entry kt | (blocks allowing it) << 14
+  __shared__ uint16_t lds_list[kMode == kSparse ? kMaxSparseTiles : 1];
+  __shared__ int lds_cnt[kWaves];
+  const uint32_t wbit = wave < 4 ? 1u : 2u;
+  if (kMode == kSparse) {
+    const uint8_t* m0 = block_mask + ((size_t)bh * nqb + 2 * qt) * nkt_all;
+    const bool has1 = 2 * qt + 1 < nqb;
+    int nvis = 0;
+    for (int c0 = 0; c0 < nkt_all; c0 += kThreads) {
+      const int kt = c0 + tid;
+      uint32_t f = 0;
+      if (kt < nkt_all) f = (m0[kt] ? 1u : 0u) | ((has1 && m0[nkt_all + kt]) ? 2u : 0u);
+      const unsigned long long bal = __ballot(f != 0);
+      if (lane == 0) lds_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int off = nvis;
+      for (int w = 0; w < wave; ++w) off += lds_cnt[w];
+      if (f) lds_list[off + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)(kt | (f << 14));
+      for (int w = 0; w < kWaves; ++w) nvis += lds_cnt[w];
+      __syncthreads();
+    }
+    nkt = __builtin_amdgcn_readfirstlane(nvis);
+    if (nkt == 0) {  // no allowed key for any row of this workgroup: zeros
+      if (qok)
+        for (int d = 0; d < kHeadDim; d += 8)
+          *reinterpret_cast<u32x4*>(Oh + (size_t)qrow * kHeadDim + d) = u32x4{0u, 0u, 0u, 0u};
+      return;
+    }
+  }
+  // key tile of loop step t (clamped: steps past the end reload the last one)
+  auto tile_of = [&](int t) __attribute__((always_inline)) {
+    t = min(t, nkt - 1);
+    return kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(lds_list[t] & 0x3fffu)) : t;
+  };
+
   // ---- DMA: one 1 KB load per wave per tile and tensor ----
   // K: wave w fills tile rows 8w .. 8w+7; lane i writes physical chunk i%8 of
   // row 8w + i/8 and fetches the logical chunk the swizzle maps there.
@@ -132,15 +181,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const int kgo = krow * kHeadDim + 16 * ((lane & 7) ^ (krow & 7));
   const uint32_t wslice = (uint32_t)wave * 1024;
   auto issue_k = [&](int t, const void* buf) __attribute__((always_inline)) {
-    t = min(t, nkt - 1);  // past the end: reload the last tile into a free buffer
+    t = tile_of(t);  // past the end: reload the last tile into a free buffer
     const int key0 = t * kBc;
     const char* src = K8h + (size_t)key0 * kHeadDim;
     int go = kgo;
-    if (tail && t == nkt - 1) go = (min(key0 + krow, S - 1) - key0) * kHeadDim + 16 * ((lane & 7) ^ (krow & 7));
+    if (tail && t == nkt_all - 1) go = (min(key0 + krow, S - 1) - key0) * kHeadDim + 16 * ((lane & 7) ^ (krow & 7));
     dma16(src, (uint32_t)go, lds_addr(buf) + wslice);
   };
   auto issue_v = [&](int t, const void* buf) __attribute__((always_inline)) {
-    t = min(t, nkt - 1);
+    t = tile_of(t);
     dma16(V8h + (size_t)t * kTileBytes, (uint32_t)(wslice + 16 * lane), lds_addr(buf) + wslice);
   };
   // K operand of key block kb, channel step kk: lane (key 32kb + col, half)
@@ -164,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     qf[kk] = join(ld16(p, qok), ld16(p + 16, qok));
   }
   // all 32 queries of a wave sit in one 64-token scale block
-  const float qsc = q_scale[(size_t)bh * nkt + min(qrow, S - 1) / kBc] * c;
+  const float qsc = q_scale[(size_t)bh * nkt_all + min(qrow, S - 1) / kBc] * c;
 
   // dec(q8) in bf16 (exact) as the B operand of the K-mean MFMAs (lane:
   // query col, channels 16kk + 8half .. +7).  With V block means it is parked
@@ -179,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     for (int e = 0; e < 8; ++e) qh_reg[kk][e] = (__bf16)e4m3_value((w[e >> 2] >> (8 * (e & 3))) & 255u);
     if (kVBlock) lds_qh[wave][kk][lane] = qh_reg[kk];
   }
-  const int nbm = kBlockMean ? nkt : 1;
+  const int nbm = kBlockMean ? nkt_all : 1;
   const float* kmh = k_mean + (size_t)bh * nbm * kHeadDim;
   // dec(q8_i) . k_mean_b for b = b0 .. b0+31 (clamped to the last block),
   // written to this wave's LDS slots lds_comp[wave][b - b0][query].  Each
@@ -189,7 +238,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     f32x16 cm;
 #pragma unroll
     for (int i = 0; i < 16; ++i) cm[i] = 0.f;
-    const float* km = kmh + (size_t)min(b0 + col, nbm - 1) * kHeadDim;
+    // lane col: the K block of loop step b0 + col
+    const int kb_lane = kMode == kSparse ? (int)(lds_list[min(b0 + col, nkt - 1)] & 0x3fffu)
+                                         : min(b0 + col, nbm - 1);
+    const float* km = kmh + (size_t)kb_lane * kHeadDim;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const f32x4 a0 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half);
@@ -238,8 +290,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = t * kBc + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (key >= S) s[kb][i] = -INFINITY;
+        if (key >= lim) s[kb][i] = -INFINITY;
       }
+  };
+  // block-sparse: step t's scores -inf where this wave's query block does not
+  // allow the tile (or t is past the list), keys past S in the ragged tile
+  auto mask_sparse = [&](int t) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    uint32_t e = 0;
+    if (t < nkt) e = lds_list[t];
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int kt = (int)(e & 0x3fffu);
+    if (((e >> 14) & wbit) == 0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = -INFINITY;
+    } else if (tail && kt == nkt_all - 1) {
+      mask_tail(kt);
+    }
+  };
+  auto mask_step = [&](int t) __attribute__((always_inline)) {
+    if (kMode == kSparse)
+      mask_sparse(t);
+    else if (t * kBc + kBc > wave_lim)
+      mask_tail(t);
   };
 
   f32x16 acc[4];
@@ -253,7 +328,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
-  float m_ref = -INFINITY;
+  // finite when block-sparse: tiles scored entirely -inf before a row's first
+  // allowed key then give weight 0, not NaN
+  float m_ref = kMode == kSparse ? -1e30f : -INFINITY;
   // V block means: row sum of the drained batches; 1 / v_scale per channel
   // in LDS (it scales the means into code units for the restore MFMA)
   float l_tot = 0.f;
@@ -308,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // e = 2^(t - m) * 448 <= 448 up to the last bit of exp2, packed as E4M3.
   uint32_t pk[8];
   auto softmax_p = [&](int t) __attribute__((always_inline)) {
-    const float a = qsc * ksh[t];
+    const float a = qsc * ksh[tile_of(t)];
     const float cb = kBlockMean ? lds_comp[wave][t % kCompBlocks][col] * qsc : cb_global;
     float t8[8];
 #pragma unroll
@@ -423,9 +500,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     __builtin_amdgcn_sched_barrier(0);
     qk(kn);
     pv(vc, t);
-    // keys past S (the ragged last tile, or the tile after the last, whose
-    // scores come from reloaded data and must weigh nothing)
-    if ((t + 1) * kBc + kBc > S) mask_tail(t + 1);
+    // keys past the row limits (the ragged last tile, or the tile after the
+    // last, whose scores come from reloaded data and must weigh nothing)
+    mask_step(t + 1);
     if (kBlockMean && ((t + 1) % kCompBlocks) == 0 && t + 1 < nkt) kmean_batch(t + 1);
     __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
     __builtin_amdgcn_sched_barrier(0);
@@ -442,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   barrier();
   qk(lds_k0);
-  if (kBc > S) mask_tail(0);
+  mask_step(0);
   if (!group_a) barrier();  // group B starts one phase later
 
   // three tiles per iteration, so every ring buffer is named statically
@@ -471,7 +548,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     vload((nkt - 1) >> 5);
     vdrain();
   }
-  const float inv = 1.0f / (kVBlock ? l_tot : lacc[0]);
+  const float lsum = kVBlock ? l_tot : lacc[0];
+  // a row with no allowed key (block-sparse) has l = 0 and outputs zeros
+  const bool empty_row = kMode == kSparse && lsum == 0.f;
+  const float inv = empty_row ? 0.f : 1.0f / lsum;
   if (qok && kVBlock) {
     const float* vsh = v_scale + (size_t)bh * kHeadDim;
 #pragma unroll
@@ -494,7 +574,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * mb + 8 * g + 4 * half;
         const f32x4 vs = *reinterpret_cast<const f32x4*>(vsh + d0);
-        const f32x4 vm = *reinterpret_cast<const f32x4*>(vmh + d0);
+        f32x4 vm = *reinterpret_cast<const f32x4*>(vmh + d0);
+        if (empty_row) vm = f32x4{0.f, 0.f, 0.f, 0.f};
         u32x2 w;
         w.x = pack_bf16x2(fmaf(acc[mb][4 * g] * inv, vs[0], vm[0]),
                           fmaf(acc[mb][4 * g + 1] * inv, vs[1], vm[1]));
@@ -505,19 +586,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   }
 }
 
-template <bool kExpCast, bool kVBlock>
+template <bool kExpCast, bool kVBlock, int kMode>
 void launch_fp8(bool block_mean, unsigned blocks, hipStream_t stream, const uint8_t* q,
                 const uint8_t* k, const uint8_t* v, const float* q_scale, const float* k_scale,
                 const float* k_mean, const float* v_mean, const uint16_t* v_bmean, int nbv_pad,
-                const float* v_scale, uint16_t* out, int S, int n_qtiles, float c) {
+                const float* v_scale, uint16_t* out, int S, int n_qtiles, float c, int chunk,
+                const uint8_t* mask, int nqb) {
   if (block_mean)
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, kExpCast, kVBlock>), dim3(blocks), dim3(kThreads),
-                       0, stream, q, k, v, q_scale, k_scale, k_mean, v_mean, v_bmean, nbv_pad,
-                       v_scale, out, S, n_qtiles, c);
-  else
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, kExpCast, kVBlock>), dim3(blocks),
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, kExpCast, kVBlock, kMode>), dim3(blocks),
                        dim3(kThreads), 0, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
-                       v_bmean, nbv_pad, v_scale, out, S, n_qtiles, c);
+                       v_bmean, nbv_pad, v_scale, out, S, n_qtiles, c, chunk, mask, nqb);
+  else
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, kExpCast, kVBlock, kMode>), dim3(blocks),
+                       dim3(kThreads), 0, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
+                       v_bmean, nbv_pad, v_scale, out, S, n_qtiles, c, chunk, mask, nqb);
+}
+
+template <bool kExpCast>
+void launch_fp8_mode(bool block_mean, bool vblock, int chunk, const uint8_t* mask, unsigned blocks,
+                     hipStream_t stream, const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                     const float* q_scale, const float* k_scale, const float* k_mean,
+                     const float* v_mean, const uint16_t* v_bmean, int nbv_pad,
+                     const float* v_scale, uint16_t* out, int S, int n_qtiles, float c, int nqb) {
+  if (vblock)
+    launch_fp8<kExpCast, true, kDense>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean,
+                                       v_mean, v_bmean, nbv_pad, v_scale, out, S, n_qtiles, c, 0,
+                                       nullptr, nqb);
+  else if (mask)
+    launch_fp8<kExpCast, false, kSparse>(block_mean, blocks, stream, q, k, v, q_scale, k_scale,
+                                         k_mean, v_mean, v_bmean, nbv_pad, v_scale, out, S,
+                                         n_qtiles, c, 0, mask, nqb);
+  else if (chunk > 0)
+    launch_fp8<kExpCast, false, kCausal>(block_mean, blocks, stream, q, k, v, q_scale, k_scale,
+                                         k_mean, v_mean, v_bmean, nbv_pad, v_scale, out, S,
+                                         n_qtiles, c, chunk, nullptr, nqb);
+  else
+    launch_fp8<kExpCast, false, kDense>(block_mean, blocks, stream, q, k, v, q_scale, k_scale,
+                                        k_mean, v_mean, v_bmean, nbv_pad, v_scale, out, S, n_qtiles,
+                                        c, 0, nullptr, nqb);
 }
 
 }  // namespace
@@ -526,7 +632,8 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                const float* q_scale, const float* k_scale, const float* k_mean,
                                int k_mean_blocks, const float* v_mean, const void* v_bmean,
                                const float* v_scale, void* o, int B, int H, int S, float scale,
-                               bool expcast, hipStream_t stream) {
+                               bool expcast, int chunk, const void* block_mask,
+                               hipStream_t stream) {
   const int n_qtiles = (S + kBr - 1) / kBr;
   const unsigned blocks = (unsigned)((long long)B * H * n_qtiles);
   const int nb = (S + kBc - 1) / kBc;
@@ -537,22 +644,16 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
   uint16_t* out = static_cast<uint16_t*>(o);
   const float c = scale * kLog2e;
   const uint16_t* vbm = static_cast<const uint16_t*>(v_bmean);
+  const uint8_t* mask = static_cast<const uint8_t*>(block_mask);
   const int nbv_pad = vsmooth_blocks_padded(S);
-  if (vbm) {
-    if (expcast)
-      launch_fp8<true, true>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
-                             vbm, nbv_pad, v_scale, out, S, n_qtiles, c);
-    else
-      launch_fp8<false, true>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
-                              vbm, nbv_pad, v_scale, out, S, n_qtiles, c);
-  } else {
-    if (expcast)
-      launch_fp8<true, false>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean, v_mean,
-                              vbm, nbv_pad, v_scale, out, S, n_qtiles, c);
-    else
-      launch_fp8<false, false>(block_mean, blocks, stream, q, k, v, q_scale, k_scale, k_mean,
-                               v_mean, vbm, nbv_pad, v_scale, out, S, n_qtiles, c);
-  }
+  const int nqb = (S + 127) / 128;
+  if (expcast)
+    launch_fp8_mode<true>(block_mean, vbm != nullptr, chunk, mask, blocks, stream, q, k, v, q_scale,
+                          k_scale, k_mean, v_mean, vbm, nbv_pad, v_scale, out, S, n_qtiles, c, nqb);
+  else
+    launch_fp8_mode<false>(block_mean, vbm != nullptr, chunk, mask, blocks, stream, q, k, v,
+                           q_scale, k_scale, k_mean, v_mean, vbm, nbv_pad, v_scale, out, S,
+                           n_qtiles, c, nqb);
   return hipGetLastError();
 }
 

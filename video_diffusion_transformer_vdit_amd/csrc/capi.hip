@@ -184,7 +184,7 @@ static vdit_status fwd_fp8(const void* q8, const void* k8, const void* v8, const
                            const float* k_scale, const float* k_mean, int k_mean_blocks,
                            const float* v_mean, const void* v_bmean, const float* v_scale,
                            void* o, int B, int H, int S, int D, float scale, bool expcast,
-                           void* stream) {
+                           void* stream, int chunk = 0, const void* block_mask = nullptr) {
   VDIT_TRY(check_ptr(q8, "q8"));
   VDIT_TRY(check_ptr(k8, "k8"));
   VDIT_TRY(check_ptr(v8, "v8"));
@@ -202,9 +202,11 @@ static vdit_status fwd_fp8(const void* q8, const void* k8, const void* v8, const
   const int nb = (S + VDIT_FP8_BLOCK - 1) / VDIT_FP8_BLOCK;
   if (k_mean_blocks != 1 && k_mean_blocks != nb)
     return fail(VDIT_ERR_UNSUPPORTED, "%s", "k_mean_blocks must be 1 or ceil(S/64)");
+  if (block_mask && (S + 63) / 64 > 16384)
+    return fail(VDIT_ERR_UNSUPPORTED, "%s", "block-sparse attention supports S <= 1048576");
   return hip_result(vdit::launch_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks,
                                               v_mean, v_bmean, v_scale, o, B, H, S, scale, expcast,
-                                              static_cast<hipStream_t>(stream)));
+                                              chunk, block_mask, static_cast<hipStream_t>(stream)));
 }
 
 vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
@@ -224,6 +226,21 @@ vdit_status vdit_attn_fwd_fp8_expcast(const void* q8, const void* k8, const void
   if (!v_mean) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: v_mean");
   return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, nullptr, v_scale, o,
                  B, H, S, D, scale, true, stream);
+}
+
+vdit_status vdit_attn_fwd_fp8_masked(const void* q8, const void* k8, const void* v8,
+                                     const float* q_scale, const float* k_scale,
+                                     const float* k_mean, int k_mean_blocks, const float* v_mean,
+                                     const float* v_scale, void* o, int B, int H, int S, int D,
+                                     float scale, int chunk, const void* block_mask, int expcast,
+                                     void* stream) {
+  if (!v_mean) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: v_mean");
+  if (chunk < 0) return fail(VDIT_ERR_INVALID_ARG, "%s", "chunk must be >= 0");
+  if (chunk > 0 && block_mask)
+    return fail(VDIT_ERR_INVALID_ARG, "%s", "give either chunk or block_mask, not both");
+  if (expcast != 0 && expcast != 1) return fail(VDIT_ERR_INVALID_ARG, "%s", "expcast must be 0 or 1");
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, nullptr, v_scale, o,
+                 B, H, S, D, scale, expcast == 1, stream, chunk, block_mask);
 }
 
 vdit_status vdit_attn_fwd_fp8_vsmooth(const void* q8, const void* k8, const void* v8,

@@ -33,7 +33,8 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                const float* k_mean, int k_mean_blocks,
                                const float* v_mean, const void* v_bmean,
                                const float* v_scale, void* o, int B, int H, int S, float scale,
-                               bool expcast, hipStream_t stream);
+                               bool expcast, int chunk, const void* block_mask,
+                               hipStream_t stream);
 
 // V-Smooth Group: k-means of V tokens and the stable cluster permutation
 constexpr int kGroupMaxClusters = 4096;
