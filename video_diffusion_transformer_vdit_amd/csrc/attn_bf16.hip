@@ -74,6 +74,24 @@ constexpr int kDense = 0, kCausal = 1, kSparse = 2;
 constexpr int kSparseQBlock = 128;
 constexpr int kMaxSparseTiles = 16384;  // key tiles per head (S <= 1,048,576)
 
+// Matrix-phase schedule: the reads of the first kLead operands, then MFMA i
+// followed by the reads of operand i + kLead (operands 0-15 are one K read
+// each, 16-31 two V reads each), then the last kLead MFMAs.
+constexpr int kLead = 6;
+constexpr int reads_of(int op) { return op < 16 ? 1 : 2; }
+constexpr int reads_before(int n) { return n <= 0 ? 0 : reads_of(n - 1) + reads_before(n - 1); }
+template <int L, int I = 0>
+__device__ __forceinline__ void sched_reads_ahead() {
+  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, reads_before(L), 0);
+  if constexpr (I < 32 - L) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, reads_of(I + L), 0);
+    sched_reads_ahead<L, I + 1>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, L, 0);
+  }
+}
+
 template <int kMode>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -284,13 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   // Reference update and (rare) rescale.  In the common case only the
   // lane-local maximum is formed and compared with the reference.
   auto update_max = [&]() __attribute__((always_inline)) {
-    float t8[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      t8[u] = fmaxf(fmaxf(s[u >> 2][4 * (u & 3)], s[u >> 2][4 * (u & 3) + 1]),
-                    fmaxf(s[u >> 2][4 * (u & 3) + 2], s[u >> 2][4 * (u & 3) + 3]));
-    const float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
-                           fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7]))) * c;
+    const float mx = max_of_32(s[0], s[1]) * c;
     if (__ballot(mx > m_ref) != 0ull) {
       // rare: keep it a real branch rather than 64 multiplies per tile
       asm volatile("" ::: "memory");
@@ -378,23 +390,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     qk(kn);
     pv(vc);
-    // Keep every operand read six MFMAs ahead of its use across the 32 MFMAs
-    // of the phase (16 K operands of one read, then 16 V operands of two):
-    // the default schedule reads each operand just before its MFMA, which
-    // leaves a lone wave waiting on LDS latency.  Six K reads first, then
-    // MFMA i followed by the reads of operand i + 6.
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < 10; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    // Keep every operand read kLead MFMAs ahead of its use across the 32
+    // MFMAs of the phase (16 K operands of one read, then 16 V operands of
+    // two): the default schedule reads each operand just before its MFMA,
+    // which leaves a lone wave waiting on LDS latency.
+    sched_reads_ahead<kLead>();
     // keys past S (the ragged last tile, or the tile after the last, whose
     // scores come from reloaded data and must weigh nothing)
     if (kMode == kSparse)

@@ -102,13 +102,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint16_t* __restrict__ v_bmean, int nbv_pad, const float* __restrict__ v_scale,
     uint16_t* __restrict__ O, int S, int n_qtiles, float c, int chunk,
     const uint8_t* __restrict__ block_mask, int nqb) {
-  // three-deep rings of K and V tiles, one LDS object per buffer
+  // four-deep rings of K and V tiles (three-deep with V block means, whose
+  // LDS holds the bf16 copy of Q as well), one LDS object per buffer
+  constexpr int kRing = kVBlock ? 3 : 4;
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k3[kRing == 4 ? kTileBytes : 1];
   __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v3[kRing == 4 ? kTileBytes : 1];
   __shared__ float lds_comp[kWaves][kCompBlocks][32];
   __shared__ __attribute__((aligned(16))) float lds_ivs[kHeadDim];  // 1 / v_scale (V block means only)
   __shared__ bf16x8 lds_qh[kWaves][8][64];  // dec(q8) in bf16, per lane (K-mean term)
@@ -326,8 +330,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   f32x16 lacc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
+  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
+  // opaque from here on: kept in its eight registers rather than copied back
+  // from one register before every row-sum MFMA
+  if (!kVBlock) asm volatile("" : "+v"(ones));
   // finite when block-sparse: tiles scored entirely -inf before a row's first
   // allowed key then give weight 0, not NaN
   float m_ref = kMode == kSparse ? -1e30f : -INFINITY;
@@ -387,13 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   auto softmax_p = [&](int t) __attribute__((always_inline)) {
     const float a = qsc * ksh[tile_of(t)];
     const float cb = kBlockMean ? lds_comp[wave][t % kCompBlocks][col] * qsc : cb_global;
-    float t8[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      t8[u] = fmaxf(fmaxf(s[u >> 2][4 * (u & 3)], s[u >> 2][4 * (u & 3) + 1]),
-                    fmaxf(s[u >> 2][4 * (u & 3) + 2], s[u >> 2][4 * (u & 3) + 3]));
-    const float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
-                           fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
+    const float mx = max_of_32(s[0], s[1]);
     const float mnew = fmaf(mx, a, cb);
     if (__ballot(mnew > m_ref) != 0ull) {
       // rare: keep it a real branch rather than 80 multiplies per tile
@@ -416,7 +417,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p], a8, b8), 0, 0u);
+          // all four bytes are written: start from the first input's bits
+          const float x0 = fmaf(s[kb][4 * p], a8, b8);
+          uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(x0, 0, __float_as_uint(x0));
           w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 1], a8, b8), 1, w);
           w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 2], a8, b8), 2, w);
           pk[4 * kb + p] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 3], a8, b8), 3, w);
@@ -431,7 +434,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
           const float e1 = exp2_fast(fmaf(s[kb][4 * p + 1], a, bias));
           const float e2 = exp2_fast(fmaf(s[kb][4 * p + 2], a, bias));
           const float e3 = exp2_fast(fmaf(s[kb][4 * p + 3], a, bias));
-          uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+          // the second convert fills the high half: start from e0's bits, not a zeroed register
+          uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, (int)__float_as_uint(e0), false);
           pk[4 * kb + p] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
         }
     }
@@ -473,10 +477,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // O += P8(t) V(t) (MFMA), plus the K-mean batch for the next 32 tiles when
   // tile t+1 starts one.  Waves 4-7 run one phase behind waves 0-3; a barrier
   // ends every phase.  At the start of P2(t) every wave issues its share of
-  // K(t+3) and V(t+2), into the buffers of K(t) and V(t-1), which both groups
-  // have finished reading by then; every wave waits for all but its newest
-  // two loads before each barrier.
+  // K(t+kRing) and V(t+kRing-1), into the buffers of K(t) and V(t-1), which
+  // both groups have finished reading by then; every wave waits for all but
+  // its newest kRing - 2 batches before each barrier, so a load has
+  // 2 kRing - 3 phases to land.
   const bool group_a = wave < 4;
+  // all but the newest kRing - 2 batches (two loads each): a batch issued in
+  // phase 2 of step t is first read in phase 2 of step t + kRing - 1
+  auto wait_loads = [&]() __attribute__((always_inline)) {
+    if (kRing == 4)
+      __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
+  };
   auto phase1 = [&](int t) __attribute__((always_inline)) {
     if (kVBlock && (t % 32) == 0 && t > 0) vload((t >> 5) - 1);
     softmax_p(t);
@@ -484,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     // after the barrier, into the MFMA phase
     asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]), "v"(pk[4]), "v"(pk[5]),
                  "v"(pk[6]), "v"(pk[7]));
-    __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2): all but the newest batch
+    wait_loads();
     __builtin_amdgcn_sched_barrier(0);
     barrier();
   };
@@ -495,8 +508,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       vdrain();
       __builtin_amdgcn_sched_barrier(0);
     }
-    issue_k(t + 3, kfill);
-    issue_v(t + 2, vfill);
+    issue_k(t + kRing, kfill);
+    issue_v(t + kRing - 1, vfill);
     __builtin_amdgcn_sched_barrier(0);
     qk(kn);
     pv(vc, t);
@@ -504,17 +517,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     // last, whose scores come from reloaded data and must weigh nothing)
     mask_step(t + 1);
     if (kBlockMean && ((t + 1) % kCompBlocks) == 0 && t + 1 < nkt) kmean_batch(t + 1);
-    __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
+    wait_loads();
     __builtin_amdgcn_sched_barrier(0);
     barrier();
   };
 
-  // ---- prologue: K(0..2), V(0..1) in flight; S(0) ----
+  // ---- prologue: K(0..kRing-1), V(0..kRing-2) in flight; S(0) ----
   issue_k(0, lds_k0);
   issue_v(0, lds_v0);
   issue_k(1, lds_k1);
   issue_v(1, lds_v1);
   issue_k(2, lds_k2);
+  if (kRing == 4) {
+    issue_v(2, lds_v2);
+    issue_k(3, lds_k3);
+  }
   if (kBlockMean) kmean_batch(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   barrier();
@@ -522,23 +539,50 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   mask_step(0);
   if (!group_a) barrier();  // group B starts one phase later
 
-  // three tiles per iteration, so every ring buffer is named statically
+  // kRing tiles per iteration, so every ring buffer is named statically.
+  // Step t reads K(t+1) and V(t) and refills the buffers of K(t) and V(t-1)
+  // with K(t+kRing) and V(t+kRing-1).
   int t = 0;
-  for (; t + 3 <= nkt; t += 3) {
-    phase1(t);
-    phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
-    phase1(t + 1);
-    phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
-    phase1(t + 2);
-    phase2(t + 2, lds_k0, lds_v2, lds_k2, lds_v1);
-  }
-  if (t < nkt) {
-    phase1(t);
-    phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
-  }
-  if (t + 1 < nkt) {
-    phase1(t + 1);
-    phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+  if (kRing == 4) {
+    for (; t + 4 <= nkt; t += 4) {
+      phase1(t);
+      phase2(t, lds_k1, lds_v0, lds_k0, lds_v3);
+      phase1(t + 1);
+      phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+      phase1(t + 2);
+      phase2(t + 2, lds_k3, lds_v2, lds_k2, lds_v1);
+      phase1(t + 3);
+      phase2(t + 3, lds_k0, lds_v3, lds_k3, lds_v2);
+    }
+    if (t < nkt) {
+      phase1(t);
+      phase2(t, lds_k1, lds_v0, lds_k0, lds_v3);
+    }
+    if (t + 1 < nkt) {
+      phase1(t + 1);
+      phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+    }
+    if (t + 2 < nkt) {
+      phase1(t + 2);
+      phase2(t + 2, lds_k3, lds_v2, lds_k2, lds_v1);
+    }
+  } else {
+    for (; t + 3 <= nkt; t += 3) {
+      phase1(t);
+      phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
+      phase1(t + 1);
+      phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+      phase1(t + 2);
+      phase2(t + 2, lds_k0, lds_v2, lds_k2, lds_v1);
+    }
+    if (t < nkt) {
+      phase1(t);
+      phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
+    }
+    if (t + 1 < nkt) {
+      phase1(t + 1);
+      phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+    }
   }
   if (group_a) barrier();  // matches group B's extra one
   // no DMA may still be writing this workgroup's LDS when it exits

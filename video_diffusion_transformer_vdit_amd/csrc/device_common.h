@@ -88,6 +88,30 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
 }
 
+// max(a, b, c) as one v_max3_f32.  Written as asm because in IEEE mode the
+// compiler first quiets every operand it cannot prove canonical (an MFMA
+// result, say) with a v_max of its own; the scores here are never NaN.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// maximum of the 32 values of two 16-register score blocks: 16 v_max3_f32
+__device__ __forceinline__ float max_of_32(const f32x16& a, const f32x16& b) {
+  float m[12];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) m[i] = max3_raw(a[3 * i], a[3 * i + 1], a[3 * i + 2]);
+  m[5] = max3_raw(a[15], b[0], b[1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[6 + i] = max3_raw(b[2 + 3 * i], b[3 + 3 * i], b[4 + 3 * i]);
+  m[10] = b[14];
+  m[11] = b[15];
+  const float r0 = max3_raw(m[0], m[1], m[2]), r1 = max3_raw(m[3], m[4], m[5]);
+  const float r2 = max3_raw(m[6], m[7], m[8]), r3 = max3_raw(m[9], m[10], m[11]);
+  return max3_raw(max3_raw(r0, r1, r2), r3, r3);
+}
+
 // max / sum of the values held by lanes l and l ^ 32
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
