@@ -379,3 +379,25 @@ def test_fp8_masks_full_size_sampled():
             ref = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows, allowed=allowed,
                                                 p_cast="expcast" if ec else "exp")
             check_model(got[i], ref, f"fp8 720p {kind} expcast={ec} head {h}")
+
+
+@pytest.mark.parametrize("p_cast", ["exp", "expcast"])
+@pytest.mark.parametrize("kind", ["causal", "sparse"])
+def test_fp8_masks_with_one_k_mean_per_head(kind, p_cast):
+    """Key masks on the pre-pass with one K mean per head (k_mean_blocks = 1):
+    every visited tile takes that one mean."""
+    import torch
+    S = 1000
+    q, k, v = masked_inputs(S, 97, H=3)
+    zo = ofp8.quantize(q, k, v, k_mean="global")
+    assert zo["k_mean"].shape[2] == 1
+    if kind == "causal":
+        kw, allowed_of = {"chunk": 300}, (lambda b, h: oa.block_causal_allowed(S, 300))
+    else:
+        mask = random_tile_mask(1, 3, S, 0.3, seed=11)
+        kw = {"block_mask": torch.from_numpy(mask).cuda()}
+        allowed_of = lambda b, h: oa.tile_mask_allowed(S, 128, 64, mask[b, h])
+    log(f"fp8 {kind} with one K mean per head, {p_cast}")
+    o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE, expcast=p_cast == "expcast", **kw)
+    torch.cuda.synchronize()
+    check_model(f32_of(o), masked_model(zo, allowed_of, p_cast), f"fp8 {kind} global k_mean {p_cast}")

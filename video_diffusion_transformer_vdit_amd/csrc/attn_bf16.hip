@@ -166,6 +166,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     t = min(t, nkt - 1);
     return kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(lds_list[t] & 0x3fffu)) : t;
   };
+  // block-sparse: the list entries that the matrix phase of step t needs (the
+  // tiles of K(t+3) and V(t+2), the mask of step t+1), read in the
+  // exponential phase before it so that the matrix phase does not wait on LDS
+  uint32_t pre_k = 0, pre_v = 0, pre_m = 0;
+  auto prefetch_list = [&](int t) __attribute__((always_inline)) {
+    if (kMode == kSparse) {
+      pre_k = lds_list[min(t + 3, nkt - 1)];
+      pre_v = lds_list[min(t + 2, nkt - 1)];
+      pre_m = t + 1 < nkt ? (uint32_t)lds_list[t + 1] : 0u;
+    }
+  };
 
   // ---- per-lane constant offsets ----
   // K and V loads: wave w, load i covers tile rows 8w + 4i + lane/16; lane
@@ -196,8 +207,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     voff[mb] = vrow * kRowBytes + 16 * (4 * (mb ^ (s16 >> 2)) + vx) + 8 * (s16 & 1);
 
   const uint32_t wslice = (uint32_t)wave * (4 * kLoadsPerWave * kRowBytes);
+  // DMA of key tile t (an index into K and V, not a loop step)
   auto issue_k = [&](int t, const void* buf) __attribute__((always_inline)) {
-    t = tile_of(t);  // past the end: reload the last tile into a free buffer
     const int key0 = t * kBc;
     const char* src = Kh + (size_t)key0 * kRowBytes;
     const uint32_t dst = lds_addr(buf) + wslice;
@@ -215,7 +226,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     }
   };
   auto issue_v = [&](int t, const void* buf) __attribute__((always_inline)) {
-    t = tile_of(t);
     const int key0 = t * kBc;
     const char* src = Vh + (size_t)key0 * kRowBytes;
     const uint32_t dst = lds_addr(buf) + wslice;
@@ -273,10 +283,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   };
   // block-sparse: step t's scores -inf where this wave's query block does not
   // allow the tile (or t is past the list), keys past S in the ragged tile
-  auto mask_sparse = [&](int t) __attribute__((always_inline)) {
+  auto mask_sparse = [&](uint32_t e) __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
-    uint32_t e = 0;
-    if (t < nkt) e = lds_list[t];
     e = __builtin_amdgcn_readfirstlane(e);
     const int kt = (int)(e & 0x3fffu);
     if (((e >> 14) & wbit) == 0) {
@@ -370,7 +378,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   // every barrier, so a load has at least two phases to land before the
   // barrier that precedes its first use.
   const bool group_a = wave < 4;
-  auto phase1 = [&]() __attribute__((always_inline)) {
+  auto phase1 = [&](int t) __attribute__((always_inline)) {
+    prefetch_list(t);
     update_max();
     softmax_p();
     // consume P here: otherwise the exponentials are moved to their use
@@ -385,8 +394,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   };
   auto phase2 = [&](int t, const char* kn, const char* vc, const void* kfill, const void* vfill)
                     __attribute__((always_inline)) {
-    issue_k(t + 3, kfill);
-    issue_v(t + 2, vfill);
+    // steps past the end reload the last tile into a free buffer
+    issue_k(kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(pre_k & 0x3fffu)) : tile_of(t + 3),
+            kfill);
+    issue_v(kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(pre_v & 0x3fffu)) : tile_of(t + 2),
+            vfill);
     __builtin_amdgcn_sched_barrier(0);
     qk(kn);
     pv(vc);
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
     // keys past S (the ragged last tile, or the tile after the last, whose
     // scores come from reloaded data and must weigh nothing)
     if (kMode == kSparse)
-      mask_sparse(t + 1);
+      mask_sparse(pre_m);
     else if ((t + 1) * kBc + kBc > wave_lim)
       mask_tail(t + 1);
     __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
@@ -407,16 +419,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   };
 
   // ---- prologue: K(0..2), V(0..1) in flight; S(0) ----
-  issue_k(0, lds_k0);
-  issue_v(0, lds_v0);
-  issue_k(1, lds_k1);
-  issue_v(1, lds_v1);
-  issue_k(2, lds_k2);
+  issue_k(tile_of(0), lds_k0);
+  issue_v(tile_of(0), lds_v0);
+  issue_k(tile_of(1), lds_k1);
+  issue_v(tile_of(1), lds_v1);
+  issue_k(tile_of(2), lds_k2);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   barrier();
   qk(lds_k0);
   if (kMode == kSparse)
-    mask_sparse(0);
+    mask_sparse(lds_list[0]);
   else if (kBc > wave_lim)
     mask_tail(0);
   if (!group_a) barrier();  // group B starts one phase later
@@ -424,19 +436,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   // three tiles per iteration, so every ring buffer is named statically
   int t = 0;
   for (; t + 3 <= nkt; t += 3) {
-    phase1();
+    phase1(t);
     phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
-    phase1();
+    phase1(t + 1);
     phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
-    phase1();
+    phase1(t + 2);
     phase2(t + 2, lds_k0, lds_v2, lds_k2, lds_v1);
   }
   if (t < nkt) {
-    phase1();
+    phase1(t);
     phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
   }
   if (t + 1 < nkt) {
-    phase1();
+    phase1(t + 1);
     phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
   }
   if (group_a) barrier();  // matches group B's extra one

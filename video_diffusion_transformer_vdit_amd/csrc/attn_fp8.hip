@@ -177,6 +177,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     t = min(t, nkt - 1);
     return kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(lds_list[t] & 0x3fffu)) : t;
   };
+  // block-sparse: the list entries that the matrix phase of step t needs (the
+  // tiles of K(t+kRing) and V(t+kRing-1), the mask of step t+1, which is
+  // also the K-scale tile of the next exponential phase), read in the
+  // exponential phase before it
+  uint32_t pre_k = 0, pre_v = 0, pre_m = 0;
 
   // ---- DMA: one 1 KB load per wave per tile and tensor ----
   // K: wave w fills tile rows 8w .. 8w+7; lane i writes physical chunk i%8 of
@@ -184,8 +189,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const int krow = 8 * wave + (lane >> 3);
   const int kgo = krow * kHeadDim + 16 * ((lane & 7) ^ (krow & 7));
   const uint32_t wslice = (uint32_t)wave * 1024;
+  // DMA of key tile t (an index into K and V, not a loop step)
   auto issue_k = [&](int t, const void* buf) __attribute__((always_inline)) {
-    t = tile_of(t);  // past the end: reload the last tile into a free buffer
     const int key0 = t * kBc;
     const char* src = K8h + (size_t)key0 * kHeadDim;
     int go = kgo;
@@ -193,7 +198,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     dma16(src, (uint32_t)go, lds_addr(buf) + wslice);
   };
   auto issue_v = [&](int t, const void* buf) __attribute__((always_inline)) {
-    t = tile_of(t);
     dma16(V8h + (size_t)t * kTileBytes, (uint32_t)(wslice + 16 * lane), lds_addr(buf) + wslice);
   };
   // K operand of key block kb, channel step kk: lane (key 32kb + col, half)
@@ -242,9 +246,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     f32x16 cm;
 #pragma unroll
     for (int i = 0; i < 16; ++i) cm[i] = 0.f;
-    // lane col: the K block of loop step b0 + col
-    const int kb_lane = kMode == kSparse ? (int)(lds_list[min(b0 + col, nkt - 1)] & 0x3fffu)
-                                         : min(b0 + col, nbm - 1);
+    // lane col: the K block of loop step b0 + col (the one mean of the head
+    // without block means)
+    const int kb_lane = !kBlockMean         ? 0
+                        : kMode == kSparse ? (int)(lds_list[min(b0 + col, nkt - 1)] & 0x3fffu)
+                                           : min(b0 + col, nbm - 1);
     const float* km = kmh + (size_t)kb_lane * kHeadDim;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -299,10 +305,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   };
   // block-sparse: step t's scores -inf where this wave's query block does not
   // allow the tile (or t is past the list), keys past S in the ragged tile
-  auto mask_sparse = [&](int t) __attribute__((always_inline)) {
+  auto mask_sparse = [&](uint32_t e) __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
-    uint32_t e = 0;
-    if (t < nkt) e = lds_list[t];
     e = __builtin_amdgcn_readfirstlane(e);
     const int kt = (int)(e & 0x3fffu);
     if (((e >> 14) & wbit) == 0) {
@@ -314,9 +318,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       mask_tail(kt);
     }
   };
-  auto mask_step = [&](int t) __attribute__((always_inline)) {
+  // (block-sparse: e is the list entry of step t, 0 past the list)
+  auto mask_step = [&](int t, uint32_t e) __attribute__((always_inline)) {
     if (kMode == kSparse)
-      mask_sparse(t);
+      mask_sparse(e);
     else if (t * kBc + kBc > wave_lim)
       mask_tail(t);
   };
@@ -392,7 +397,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // e = 2^(t - m) * 448 <= 448 up to the last bit of exp2, packed as E4M3.
   uint32_t pk[8];
   auto softmax_p = [&](int t) __attribute__((always_inline)) {
-    const float a = qsc * ksh[tile_of(t)];
+    // (block-sparse: pre_m holds step t's list entry here)
+    const float a = qsc * ksh[kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(pre_m & 0x3fffu))
+                                               : min(t, nkt - 1)];
     const float cb = kBlockMean ? lds_comp[wave][t % kCompBlocks][col] * qsc : cb_global;
     const float mx = max_of_32(s[0], s[1]);
     const float mnew = fmaf(mx, a, cb);
@@ -497,6 +504,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     // after the barrier, into the MFMA phase
     asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]), "v"(pk[4]), "v"(pk[5]),
                  "v"(pk[6]), "v"(pk[7]));
+    // (after the softmax, which reads step t's entry from pre_m)
+    if (kMode == kSparse) {
+      pre_k = lds_list[min(t + kRing, nkt - 1)];
+      pre_v = lds_list[min(t + kRing - 1, nkt - 1)];
+      pre_m = t + 1 < nkt ? (uint32_t)lds_list[t + 1] : 0u;
+    }
     wait_loads();
     __builtin_amdgcn_sched_barrier(0);
     barrier();
@@ -508,14 +521,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       vdrain();
       __builtin_amdgcn_sched_barrier(0);
     }
-    issue_k(t + kRing, kfill);
-    issue_v(t + kRing - 1, vfill);
+    // steps past the end reload the last tile into a free buffer
+    issue_k(kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(pre_k & 0x3fffu)) : tile_of(t + kRing),
+            kfill);
+    issue_v(kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(pre_v & 0x3fffu))
+                             : tile_of(t + kRing - 1),
+            vfill);
     __builtin_amdgcn_sched_barrier(0);
     qk(kn);
     pv(vc, t);
     // keys past the row limits (the ragged last tile, or the tile after the
     // last, whose scores come from reloaded data and must weigh nothing)
-    mask_step(t + 1);
+    mask_step(t + 1, pre_m);
     if (kBlockMean && ((t + 1) % kCompBlocks) == 0 && t + 1 < nkt) kmean_batch(t + 1);
     wait_loads();
     __builtin_amdgcn_sched_barrier(0);
@@ -523,20 +540,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   };
 
   // ---- prologue: K(0..kRing-1), V(0..kRing-2) in flight; S(0) ----
-  issue_k(0, lds_k0);
-  issue_v(0, lds_v0);
-  issue_k(1, lds_k1);
-  issue_v(1, lds_v1);
-  issue_k(2, lds_k2);
+  issue_k(tile_of(0), lds_k0);
+  issue_v(tile_of(0), lds_v0);
+  issue_k(tile_of(1), lds_k1);
+  issue_v(tile_of(1), lds_v1);
+  issue_k(tile_of(2), lds_k2);
   if (kRing == 4) {
-    issue_v(2, lds_v2);
-    issue_k(3, lds_k3);
+    issue_v(tile_of(2), lds_v2);
+    issue_k(tile_of(3), lds_k3);
   }
   if (kBlockMean) kmean_batch(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   barrier();
   qk(lds_k0);
-  mask_step(0);
+  if (kMode == kSparse) pre_m = lds_list[0];
+  mask_step(0, pre_m);
   if (!group_a) barrier();  // group B starts one phase later
 
   // kRing tiles per iteration, so every ring buffer is named statically.
