@@ -114,6 +114,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) char lds_v2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v3[kRing == 4 ? kTileBytes : 1];
   __shared__ float lds_comp[kWaves][kCompBlocks][32];
+  constexpr bool kStageKm = kBlockMean && !kVBlock;
+  __shared__ __attribute__((aligned(1024))) char lds_km[kStageKm ? kCompBlocks * 512 : 1];
   __shared__ __attribute__((aligned(16))) float lds_ivs[kHeadDim];  // 1 / v_scale (V block means only)
   __shared__ bf16x8 lds_qh[kWaves][8][64];  // dec(q8) in bf16, per lane (K-mean term)
 
@@ -242,26 +244,66 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // written to this wave's LDS slots lds_comp[wave][b - b0][query].  Each
   // wave reads only its own slots, after its own writes (LDS operations of
   // one wave complete in order), so no barrier is needed around them.
+  // lane col: the K block of loop step b0 + col (the one mean of the head
+  // without block means)
+  auto kmean_block = [&](int step) __attribute__((always_inline)) {
+    return !kBlockMean         ? 0
+           : kMode == kSparse ? (int)(lds_list[min(step, nkt - 1)] & 0x3fffu)
+                              : min(step, nbm - 1);
+  };
+  // Staged block means (block means without V block means): the fp32 means
+  // of a batch's 32 blocks arrive in lds_km by DMA a few steps ahead (block
+  // b in bytes 512b .. 512b+511); each wave then rewrites its four blocks in
+  // place as bf16 hi and lo halves (x ~ hi + lo to 2^-16), 16-byte chunk c of
+  // each at chunk c ^ (b % 16) of the block's first and second 256 bytes, so
+  // that the MFMA operand reads of 32 blocks hit distinct banks.
+  auto km_issue = [&](int b0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = 4 * wave + 2 * i;
+      const int kb = kmean_block(b0 + blk + (lane >> 5));
+      dma16(reinterpret_cast<const char*>(kmh), (uint32_t)(kb * kHeadDim + 4 * (lane & 31)) * 4u,
+            lds_addr(lds_km) + (uint32_t)blk * 512u);
+    }
+  };
+  auto km_convert = [&]() __attribute__((always_inline)) {
+    const int b = 4 * wave + (lane >> 4), c = lane & 15;
+    char* row = lds_km + b * 512;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(row + 32 * c);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(row + 32 * c + 16);
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = e < 4 ? x0[e] : x1[e - 4];
+      hi[e] = (__bf16)x;
+      lo[e] = (__bf16)(x - (float)hi[e]);
+    }
+    // the wave's reads above complete before these writes (one wave's LDS
+    // operations are done in order), so rewriting in place is safe
+    *reinterpret_cast<bf16x8*>(row + 16 * (c ^ (b & 15))) = hi;
+    *reinterpret_cast<bf16x8*>(row + 256 + 16 * (c ^ (b & 15))) = lo;
+  };
   auto kmean_batch = [&](int b0) __attribute__((always_inline)) {
     f32x16 cm;
 #pragma unroll
     for (int i = 0; i < 16; ++i) cm[i] = 0.f;
-    // lane col: the K block of loop step b0 + col (the one mean of the head
-    // without block means)
-    const int kb_lane = !kBlockMean         ? 0
-                        : kMode == kSparse ? (int)(lds_list[min(b0 + col, nkt - 1)] & 0x3fffu)
-                                           : min(b0 + col, nbm - 1);
-    const float* km = kmh + (size_t)kb_lane * kHeadDim;
+    const float* km = kmh + (size_t)kmean_block(b0 + col) * kHeadDim;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half + 4);
       bf16x8 hi, lo;
+      if (kStageKm) {
+        const char* row = lds_km + col * 512 + 16 * ((2 * kk + half) ^ (col & 15));
+        hi = *reinterpret_cast<const bf16x8*>(row);
+        lo = *reinterpret_cast<const bf16x8*>(row + 256);
+      } else {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(km + 16 * kk + 8 * half + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = e < 4 ? a0[e] : a1[e - 4];
-        hi[e] = (__bf16)x;
-        lo[e] = (__bf16)(x - (float)hi[e]);
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? a0[e] : a1[e - 4];
+          hi[e] = (__bf16)x;
+          lo[e] = (__bf16)(x - (float)hi[e]);
+        }
       }
       const bf16x8 qh = kVBlock ? lds_qh[wave][kk][lane] : qh_reg[kk];
       cm = mfma32x32x16_bf16(hi, qh, cm);
@@ -521,6 +563,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       vdrain();
       __builtin_amdgcn_sched_barrier(0);
     }
+    // block means of the batch that starts at step t + 4
+    if (kStageKm && ((t + 4) % kCompBlocks) == 0 && t + 4 < nkt) km_issue(t + 4);
     // steps past the end reload the last tile into a free buffer
     issue_k(kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(pre_k & 0x3fffu)) : tile_of(t + kRing),
             kfill);
@@ -533,6 +577,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     // keys past the row limits (the ragged last tile, or the tile after the
     // last, whose scores come from reloaded data and must weigh nothing)
     mask_step(t + 1, pre_m);
+    // (staged means: loaded by the end of phase 2 of step t - 1 and its
+    // barrier, converted here two steps before their batch, read after the
+    // next barrier)
+    if (kStageKm && ((t + 2) % kCompBlocks) == 0 && t + 2 < nkt) km_convert();
     if (kBlockMean && ((t + 1) % kCompBlocks) == 0 && t + 1 < nkt) kmean_batch(t + 1);
     wait_loads();
     __builtin_amdgcn_sched_barrier(0);
@@ -549,9 +597,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     issue_v(tile_of(2), lds_v2);
     issue_k(tile_of(3), lds_k3);
   }
-  if (kBlockMean) kmean_batch(0);
+  if (kStageKm) km_issue(0);
+  if (kBlockMean && !kStageKm) kmean_batch(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   barrier();
+  if (kStageKm) {
+    km_convert();
+    barrier();
+    kmean_batch(0);
+  }
   qk(lds_k0);
   if (kMode == kSparse) pre_m = lds_list[0];
   mask_step(0, pre_m);
