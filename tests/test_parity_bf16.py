@@ -327,3 +327,16 @@ def test_many_heads_small_sequence():
     for b, h in sel:
         ref = oa.attention_head(x[0][b, h], x[1][b, h], x[2][b, h], SCALE)
         check_close(got[b, h], ref, f"B={b} H={h} of 8x96", ulp_slack=True)
+
+
+def test_masks_with_two_batches():
+    """B = 2: the (batch, head) offsets of the tile map and of Q/K/V/O."""
+    B, H, S = 2, 2, 700
+    g = np.random.default_rng(123)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((B, H, S, 128)).astype(np.float32)) for _ in range(3)]
+    mask = random_mask(B, H, S, 0.3, 77)
+    log("block-sparse B=2")
+    check_close(f32_of(run_sparse(*x, mask)), sparse_ref(*x, mask), "block-sparse B=2", ulp_slack=True)
+    log("block-causal B=2")
+    ref = oa.attention(*x, SCALE, allowed=oa.block_causal_allowed(S, 200))
+    check_close(f32_of(run_causal(*x, 200)), ref, "block-causal B=2", ulp_slack=True)

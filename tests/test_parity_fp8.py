@@ -401,3 +401,25 @@ def test_fp8_masks_with_one_k_mean_per_head(kind, p_cast):
     o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE, expcast=p_cast == "expcast", **kw)
     torch.cuda.synchronize()
     check_model(f32_of(o), masked_model(zo, allowed_of, p_cast), f"fp8 {kind} global k_mean {p_cast}")
+
+
+@pytest.mark.parametrize("p_cast", ["exp", "expcast"])
+def test_fp8_two_batches_dense_and_masked(p_cast):
+    """B = 2: the (batch, head) offsets of the scales, K means, V codes, the
+    tile map and O, for full, block-causal and block-sparse attention."""
+    import torch
+    B, H, S = 2, 2, 700
+    q, k, v = masked_inputs(S, 131, B=B, H=H)
+    zo = ofp8.quantize(q, k, v, k_mean="block")
+    z = zdev(zo)
+    ec = p_cast == "expcast"
+    mask = random_tile_mask(B, H, S, 0.3, seed=13)
+    cases = (("dense", {}, lambda b, h: (lambda rows: np.ones((len(rows), S), bool))),
+             ("causal", {"chunk": 200}, lambda b, h: oa.block_causal_allowed(S, 200)),
+             ("sparse", {"block_mask": torch.from_numpy(mask).cuda()},
+              lambda b, h: oa.tile_mask_allowed(S, 128, 64, mask[b, h])))
+    for name, kw, allowed_of in cases:
+        log(f"fp8 B=2 {name} {p_cast}")
+        o = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec, **kw)
+        torch.cuda.synchronize()
+        check_model(f32_of(o), masked_model(zo, allowed_of, p_cast), f"fp8 B=2 {name} {p_cast}")
