@@ -13,8 +13,9 @@
 // k_mean) where dec(q8) is exact in bf16 and k_mean is split into a bf16 high
 // part and a bf16 residual, so two bf16 MFMAs per 16 channels give it to
 // about 2^-16 relative.  With one mean per 64-token block it is computed for
-// 32 blocks at a time and parked in LDS; with one global mean it is computed
-// once.  It is applied even when it is constant along a row: a constant shift
+// 32 blocks at a time and parked in LDS (the fp32 means of a batch reach LDS
+// by DMA a few tiles ahead and are split once per workgroup); with one
+// global mean it is computed once.  It is applied even when it is constant along a row: a constant shift
 // does not change the softmax but it does move the fp8 grid P is rounded on.
 // Softmax runs in the log2 domain with an integer running reference m
 // (the ceiling of the running row maximum): p = 2^(t - m) <= 1.  P is
@@ -40,8 +41,10 @@
 // workgroup per CU; scores transposed (S^T = K Q^T) so each lane owns one
 // query; K tiles (row-major, 16-byte chunks XOR-swizzled by key & 7) and V
 // tiles (already transposed and permuted by the pre-pass) go global -> LDS by
-// DMA into three-deep rings; waves 0-3 and 4-7 run the exponential phase and
-// the MFMA phase of each tile one phase apart (ping-pong).
+// DMA into four-deep rings (three-deep with V block means); waves 0-3 and
+// 4-7 run the exponential phase and the MFMA phase of each tile one phase
+// apart (ping-pong).  The block-causal and block-sparse key masks follow the
+// bf16 kernel's schedules.
 #include "device_common.h"
 #include "launchers.h"
 
