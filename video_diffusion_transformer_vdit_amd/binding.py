@@ -252,9 +252,9 @@ def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False, chunk=0
         if "v_bmean" in z:
             raise ValueError("key masks take the per-channel V mean pre-pass (v_mean)")
         if block_mask is not None:
-            want = (B, H, -(-S // 128), -(-S // 64))
+            want = (B, H, -(-S // SPARSE_Q_BLOCK), -(-S // SPARSE_K_TILE))
             if tuple(block_mask.shape) != want:
-                raise ValueError(f"block_mask must have shape {want}")
+                raise ValueError(f"block_mask must have shape {want}, not {tuple(block_mask.shape)}")
             if block_mask.dtype == torch.bool:
                 block_mask = block_mask.view(torch.uint8)
         mask_ptr = _dev(block_mask, torch.uint8, "block_mask") if block_mask is not None else None
