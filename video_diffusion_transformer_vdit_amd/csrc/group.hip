@@ -104,14 +104,20 @@ __global__ __launch_bounds__(64 * kAssignWaves) void group_assign_kernel(
   }
   const uint16_t* muh = ws.muh + (size_t)bh * kpad * 2 * kHeadDim;
   const float* m2 = ws.m2 + (size_t)bh * kpad;
-  // staging: thread t moves 16-byte items t and t + 512 of a chunk
+  // staging: thread t moves 16-byte items t and t + 512 of a chunk; with it
+  // come the lane's |mu|^2 values of the chunk, centroids c0 + 8ii + 4half +
+  // 0..3 (in bounds: the arrays are padded to a multiple of 32 centroids;
+  // the padding is never selected)
   u32x4 st[2];
+  f32x4 m2n[4];
   auto fetch = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = threadIdx.x + 512 * u, r = i >> 5, hl = (i >> 4) & 1, q = i & 15;
       st[u] = *reinterpret_cast<const u32x4*>(muh + ((size_t)(c0 + r) * 2 + hl) * kHeadDim + 8 * q);
     }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) m2n[ii] = *reinterpret_cast<const f32x4*>(m2 + c0 + 8 * ii + 4 * half);
   };
   auto stage = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
@@ -128,6 +134,9 @@ __global__ __launch_bounds__(64 * kAssignWaves) void group_assign_kernel(
   int b = 0;
   for (int c0 = 0; c0 < k; c0 += 32) {
     const bool more = c0 + 32 < k;
+    f32x4 m2c[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) m2c[ii] = m2n[ii];
     if (more) fetch(c0 + 32);
     // A operand: centroid c0 + col, logical chunk 2kk + half of each part
     bf16x8 ah[8], al[8];
@@ -149,15 +158,22 @@ __global__ __launch_bounds__(64 * kAssignWaves) void group_assign_kernel(
       }
       // lane holds centroids c0 + 8(i/4) + 4half + i%4 of its token, in
       // increasing order: a strict < keeps the lowest index on ties
+      if (c0 + 32 <= k) {  // a full chunk: every centroid is real
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = c0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (c < k) {
-          const float d = fmaf(-2.0f, acc[i], m2[c]);
-          if (d < best[j]) {
-            best[j] = d;
-            best_c[j] = c;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const float d = fmaf(-2.0f, acc[i], m2c[i >> 2][i & 3]);
+          const bool take = d < best[j];
+          best[j] = take ? d : best[j];
+          best_c[j] = take ? c0 + 8 * (i >> 2) + 4 * half + (i & 3) : best_c[j];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = c0 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const float d = fmaf(-2.0f, acc[i], m2c[i >> 2][i & 3]);
+          const bool take = (c < k) & (d < best[j]);
+          best[j] = take ? d : best[j];
+          best_c[j] = take ? c : best_c[j];
         }
       }
     }
