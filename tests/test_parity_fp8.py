@@ -335,12 +335,14 @@ def test_fp8_block_sparse_empty_row_blocks_give_zeros(p_cast):
     mask = random_tile_mask(1, 2, S, 0.4, seed=5)
     mask[0, 0, 1] = 0          # rows 128..255 of head 0 see nothing
     mask[0, 1, 5] = 0          # the ragged last block of head 1
+    mask[0, :, 2:4] = 0        # rows 256..511: a whole workgroup, both heads
     o = binding.vdit_attn_fwd_fp8(zdev(zo), scale=SCALE, expcast=p_cast == "expcast",
                                   block_mask=torch.from_numpy(mask).cuda())
     torch.cuda.synchronize()
     got = f32_of(o)
     assert np.all(got[0, 0, 128:256] == 0) and np.all(got[0, 1, 640:] == 0)
-    rows = np.r_[0:128, 256:640]
+    assert np.all(got[0, :, 256:512] == 0)
+    rows = np.r_[0:128, 512:640]
     ref = masked_model(zo, lambda b, h: oa.tile_mask_allowed(S, 128, 64, mask[b, h]), p_cast,
                        rows=rows)
     check_model(got[:, :, rows], ref, f"fp8 block-sparse empty blocks {p_cast}")
