@@ -189,3 +189,22 @@ def test_fp8_masked_validation():
     assert st == 1 and b"not both" in lib.vdit_last_error()
     st = lib.vdit_attn_fwd_fp8_masked(*args, 0, None, 3, None)
     assert st == 1 and b"expcast" in lib.vdit_last_error()
+    far = 1 << 40  # fake buffers far apart: no overlap at this size
+    big = 1048577
+    st = lib.vdit_attn_fwd_fp8_masked(A, A + far, A + 2 * far, A + 3 * far, A + 4 * far, A + 5 * far,
+                                      -(-big // 64), A + 6 * far, A + 7 * far, A + 8 * far,
+                                      1, 1, big, 128, 0.1, 0, A + 9 * far, 0, None)
+    assert st == 2 and b"1048576" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_masked(*args[:7], None, *args[8:], 64, None, 0, None)
+    assert st == 1 and b"v_mean" in lib.vdit_last_error()
+    st = lib.vdit_attn_fwd_fp8_masked(*args[:6], 3, *args[7:], 64, None, 0, None)
+    assert st == 2 and b"k_mean_blocks" in lib.vdit_last_error()
+
+
+def test_fp8_masks_reject_block_v_means():
+    import torch
+    z = {"q8": torch.empty((1, 1, 64, 128), dtype=torch.uint8),
+         "k_mean": torch.empty((1, 1, 1, 128)),
+         "v_bmean": torch.empty((1, 1, 128, 16), dtype=torch.bfloat16)}
+    with pytest.raises(ValueError, match="per-channel V mean"):
+        binding.vdit_attn_fwd_fp8(z, chunk=32)
