@@ -276,21 +276,26 @@ __global__ __launch_bounds__(kThreads) void quant_blocks_kernel(
   }
 }
 
-// Launch 2: one workgroup per bh; thread t < 128 owns channel t.
-// With v_bmean (block mode) thread (d, part) handles the 128-token blocks of
-// parity part: mean, its bf16 rounding, and the block's residual range.
-__global__ __launch_bounds__(kThreads) void quant_reduce_kernel(
+// Launch 2: one workgroup per bh of kReduceParts x 128 threads; thread
+// (part, d) folds channel d over the blocks b = part (mod kReduceParts), and
+// thread part = 0 combines the parts in part order.  The fp64 sums of bf16
+// values are exact, so the grouping does not change them.
+// With v_bmean (block mode) thread (part, d) handles the 128-token blocks
+// b = part (mod kReduceParts): mean, its bf16 rounding, and the block's
+// residual range.
+constexpr int kReduceParts = 8;
+__global__ __launch_bounds__(kReduceParts * kHeadDim) void quant_reduce_kernel(
     float* __restrict__ v_mean, float* __restrict__ v_scale, float* __restrict__ k_mean,
     uint16_t* __restrict__ v_bmean, int nbv_pad, Workspace ws, int S, int nb, int k_global) {
-  __shared__ float ram[2][kHeadDim];
-  __shared__ double rs[2][kHeadDim];
-  __shared__ double rk[2][kHeadDim];
-  __shared__ float rmn[2][kHeadDim], rmx[2][kHeadDim];
+  __shared__ float ram[kReduceParts][kHeadDim];
+  __shared__ double rs[kReduceParts][kHeadDim];
+  __shared__ double rk[kReduceParts][kHeadDim];
+  __shared__ float rmn[kReduceParts][kHeadDim], rmx[kReduceParts][kHeadDim];
   const int bh = blockIdx.x;
   const int d = threadIdx.x & 127, part = threadIdx.x >> 7;
   double s = 0.0, sk = 0.0;
   float mn = INFINITY, mx = -INFINITY;
-  for (int b = part; b < nb; b += 2) {
+  for (int b = part; b < nb; b += kReduceParts) {
     const size_t o = ((size_t)bh * nb + b) * kHeadDim + d;
     s += ws.v_sum[o];
     mn = fminf(mn, ws.v_min[o]);
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void quant_reduce_kernel(
     const int nbv = (S + 2 * kBlock - 1) / (2 * kBlock);
     uint16_t* vb = v_bmean + ((size_t)bh * kHeadDim + d) * nbv_pad;
     float am = 0.0f;
-    for (int b = part; b < nbv_pad; b += 2) {
+    for (int b = part; b < nbv_pad; b += kReduceParts) {
       if (b >= nbv) {
         vb[b] = 0;
         continue;
@@ -324,25 +329,30 @@ __global__ __launch_bounds__(kThreads) void quant_reduce_kernel(
     ram[part][d] = am;
   }
   __syncthreads();
-  if (part == 0 && v_bmean) {
-    float sc, inv;
-    scales_from_amax(fmaxf(ram[0][d], ram[1][d]), &sc, &inv);
-    v_scale[(size_t)bh * kHeadDim + d] = sc;
-    ws.v_inv[(size_t)bh * kHeadDim + d] = inv;
-    if (k_global) k_mean[(size_t)bh * kHeadDim + d] = (float)((rk[0][d] + rk[1][d]) / (double)S);
-  } else if (part == 0) {
-    const float mean = (float)((rs[0][d] + rs[1][d]) / (double)S);
-    const float lo = fminf(rmn[0][d], rmn[1][d]);
-    const float hi = fmaxf(rmx[0][d], rmx[1][d]);
+  if (part != 0) return;
+  double ssum = 0.0, sksum = 0.0;
+  float lo = INFINITY, hi = -INFINITY, amb = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kReduceParts; ++p) {
+    ssum += rs[p][d];
+    sksum += rk[p][d];
+    lo = fminf(lo, rmn[p][d]);
+    hi = fmaxf(hi, rmx[p][d]);
+    if (v_bmean) amb = fmaxf(amb, ram[p][d]);
+  }
+  if (k_global) k_mean[(size_t)bh * kHeadDim + d] = (float)(sksum / (double)S);
+  float sc, inv;
+  if (v_bmean) {
+    scales_from_amax(amb, &sc, &inv);
+  } else {
+    const float mean = (float)(ssum / (double)S);
     // fp32 subtraction is monotone, so this is max_j |fp32(v_j - mean)|
     const float amax = fmaxf(fabsf(__fsub_rn(hi, mean)), fabsf(__fsub_rn(lo, mean)));
-    float sc, inv;
     scales_from_amax(amax, &sc, &inv);
     v_mean[(size_t)bh * kHeadDim + d] = mean;
-    v_scale[(size_t)bh * kHeadDim + d] = sc;
-    ws.v_inv[(size_t)bh * kHeadDim + d] = inv;
-    if (k_global) k_mean[(size_t)bh * kHeadDim + d] = (float)((rk[0][d] + rk[1][d]) / (double)S);
   }
+  v_scale[(size_t)bh * kHeadDim + d] = sc;
+  ws.v_inv[(size_t)bh * kHeadDim + d] = inv;
 }
 
 // Launch 3: one workgroup per (bh, block): V residual codes, and K residual
@@ -353,7 +363,10 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
     const float* __restrict__ v_mean, const uint16_t* __restrict__ v_bmean, int nbv_pad,
     Workspace ws, int S, int nb, int k_global) {
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock][kHeadDim];  // [key][channel]
+  // codes channel-major, [channel][key], rows padded to 68 bytes so that the
+  // transposing reads below spread over the banks
+  constexpr int kRowT = kBlock + 4;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim * kRowT];
   const int bh = blockIdx.x / nb;
   const int blk = blockIdx.x - bh * nb;
   const int tid = threadIdx.x;
@@ -369,22 +382,23 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
                     : v_mean[(size_t)bh * kHeadDim + 8 * c + i];
     vi[i] = ws.v_inv[(size_t)bh * kHeadDim + 8 * c + i];
   }
+  // thread (row group rg, chunk c): keys 4rg .. 4rg+3 of channels 8c .. 8c+7,
+  // one 4-key word per channel
+  uint32_t wv[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int r = rg + 16 * p;
-    u32x2 w = {0u, 0u};
+    const int r = 4 * rg + p;
     if (r < nvalid) {
       const size_t off = head + (size_t)(row0 + r) * kHeadDim + 8 * c;
       float f[8];
       unpack8(ld16(V + off, true), f);
-      uint32_t cd[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) cd[i] = e4m3_rne(clamp448(__fmul_rn(__fsub_rn(f[i], vm[i]), vi[i])));
-      w.x = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
-      w.y = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+      for (int i = 0; i < 8; ++i)
+        wv[i] |= e4m3_rne(clamp448(__fmul_rn(__fsub_rn(f[i], vm[i]), vi[i]))) << (8 * p);
     }
-    *reinterpret_cast<u32x2*>(&tile[r][8 * c]) = w;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&tile[(8 * c + i) * kRowT + 4 * rg]) = wv[i];
   __syncthreads();
   // transpose into the kernel's tile: thread -> (channel d, physical chunk pc)
   {
@@ -394,18 +408,12 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
       const int idx = tid + kThreads * h;  // 0 .. 511
       const int d = idx >> 2, pc = idx & 3;
       const int lc = pc ^ ((d >> 2) & 3);
+      // slots 16lc + 4q + b hold keys 32(lc & 1) + 8q + 4(lc >> 1) + b: four
+      // consecutive keys, one aligned word of the channel-major tile
       uint32_t wd[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t acc = 0u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int sl = 16 * lc + 4 * q + b;  // key slot
-          const int key = 32 * ((sl >> 4) & 1) + 8 * ((sl >> 2) & 3) + 4 * (sl >> 5) + (sl & 3);
-          acc |= (uint32_t)tile[key][d] << (8 * b);
-        }
-        wd[q] = acc;
-      }
+      for (int q = 0; q < 4; ++q)
+        wd[q] = *reinterpret_cast<const uint32_t*>(&tile[d * kRowT + 32 * (lc & 1) + 8 * q + 4 * (lc >> 1)]);
       *reinterpret_cast<u32x4*>(V8t + d * kBlock + 16 * pc) = u32x4{wd[0], wd[1], wd[2], wd[3]};
     }
   }
@@ -482,7 +490,7 @@ hipError_t launch_quant_fp8(const void* q, const void* k, const void* v, void* q
   if (e != hipSuccess) return e;
   uint16_t* vbm = static_cast<uint16_t*>(v_bmean);
   const int nbv_pad = vsmooth_blocks_padded(S);
-  hipLaunchKernelGGL(quant_reduce_kernel, dim3(BH), dim3(kThreads), 0, stream, v_mean, v_scale,
+  hipLaunchKernelGGL(quant_reduce_kernel, dim3(BH), dim3(kReduceParts * kHeadDim), 0, stream, v_mean, v_scale,
                      k_mean, vbm, nbv_pad, ws, S, nb, k_global);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
