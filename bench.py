@@ -246,7 +246,8 @@ def main():
         ms_a = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o8), args.steps, args.warmup)
         ms_x = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o8, expcast=True),
                              args.steps, args.warmup)
-        prepass_bytes = w.B * w.H * w.S * w.D * (2 * 3 + 2 + 1 + 2 + 1)  # reads Q,K,V,V(again); writes 3 codes
+        # reads Q, K, V (2 B each) and V again (2 B); writes three 1-byte code tensors
+        prepass_bytes = w.B * w.H * w.S * w.D * (2 * 3 + 2 + 3)
         result["fp8"] = {
             "attention_ms": round(ms_a, 4),
             "attention_tflops": round(w.flop / (ms_a * 1e-3) / 1e12, 2),
