@@ -23,7 +23,9 @@
  *  - Arguments are validated before any HIP call.  Errors are returned, never
  *    thrown.  On VDIT_ERR_HIP the launch failed; vdit_last_error() gives the
  *    HIP error text of the calling thread's last failure.
- *  - Results are deterministic: no atomics, fixed reduction order.
+ *  - Results are deterministic: no floating-point atomics, fixed reduction
+ *    order (the grouping's histograms use integer atomics, whose counts do
+ *    not depend on order).
  */
 #ifndef VDIT_ATTN_H
 #define VDIT_ATTN_H
