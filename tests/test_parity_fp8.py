@@ -425,3 +425,39 @@ def test_fp8_two_batches_dense_and_masked(p_cast):
         o = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec, **kw)
         torch.cuda.synchronize()
         check_model(f32_of(o), masked_model(zo, allowed_of, p_cast), f"fp8 B=2 {name} {p_cast}")
+
+
+def test_fp8_deterministic_and_output_guards():
+    """Every fp8 entry point twice on the same inputs: bit-identical results,
+    and nothing written outside O (sentinel guard regions around it)."""
+    import torch
+    B, H, S = 1, 2, 777
+    q, k, v = masked_inputs(S, 151, B=B, H=H)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    mask = torch.from_numpy(random_tile_mask(B, H, S, 0.4, seed=3)).cuda()
+    n = B * H * S * 128
+    guard = 4096
+    cases = []
+    for vm in ("global", "block"):
+        z = binding.vdit_attn_quant_fp8(qd, kd, vd, v_mean=vm)
+        z2 = binding.vdit_attn_quant_fp8(qd, kd, vd, v_mean=vm)
+        torch.cuda.synchronize()
+        for key in z:
+            if key != "workspace":
+                assert torch.equal(z[key], z2[key]), f"pre-pass {vm} {key}"
+        for ec in (False, True):
+            cases.append((f"{vm} expcast={ec}", z, dict(expcast=ec)))
+            if vm == "global":
+                cases.append((f"causal expcast={ec}", z, dict(expcast=ec, chunk=300)))
+                cases.append((f"sparse expcast={ec}", z, dict(expcast=ec, block_mask=mask)))
+    for name, z, kw in cases:
+        log(f"fp8 determinism {name}")
+        outs = []
+        for _ in range(2):
+            buf = torch.full((n + 2 * guard,), -7.0, dtype=torch.bfloat16, device="cuda")
+            o = buf[guard:guard + n].view(B, H, S, 128)
+            binding.vdit_attn_fwd_fp8(z, scale=SCALE, o=o, **kw)
+            torch.cuda.synchronize()
+            assert bool((buf[:guard] == -7.0).all()) and bool((buf[guard + n:] == -7.0).all()), name
+            outs.append(o.view(torch.int16).clone())
+        assert torch.equal(outs[0], outs[1]), name
