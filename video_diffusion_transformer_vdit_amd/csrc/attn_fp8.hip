@@ -105,9 +105,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint16_t* __restrict__ v_bmean, int nbv_pad, const float* __restrict__ v_scale,
     uint16_t* __restrict__ O, int S, int n_qtiles, float c, int chunk,
     const uint8_t* __restrict__ block_mask, int nqb) {
-  // four-deep rings of K and V tiles (three-deep with V block means, whose
-  // LDS holds the bf16 copy of Q as well), one LDS object per buffer
-  constexpr int kRing = kVBlock ? 3 : 4;
+  // four-deep rings of K and V tiles, one LDS object per buffer
+  constexpr int kRing = 4;
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k2[kTileBytes];
@@ -117,10 +116,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) char lds_v2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v3[kRing == 4 ? kTileBytes : 1];
   __shared__ float lds_comp[kWaves][kCompBlocks][32];
-  constexpr bool kStageKm = kBlockMean && !kVBlock;
+  constexpr bool kStageKm = kBlockMean;
   __shared__ __attribute__((aligned(1024))) char lds_km[kStageKm ? kCompBlocks * 512 : 1];
   __shared__ __attribute__((aligned(16))) float lds_ivs[kHeadDim];  // 1 / v_scale (V block means only)
-  __shared__ bf16x8 lds_qh[kWaves][8][64];  // dec(q8) in bf16, per lane (K-mean term)
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qtiles;
@@ -228,18 +226,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // all 32 queries of a wave sit in one 64-token scale block
   const float qsc = q_scale[(size_t)bh * nkt_all + min(qrow, S - 1) / kBc] * c;
 
-  // dec(q8) in bf16 (exact) as the B operand of the K-mean MFMAs (lane:
-  // query col, channels 16kk + 8half .. +7).  With V block means it is parked
-  // in LDS (needed once per 32 tiles, it would hold 32 registers that the
-  // restore needs); otherwise it stays in registers.
+  // dec(q8) in bf16 (exact: every E4M3 value is a bf16 value) as the B
+  // operand of the K-mean MFMAs (lane: query col, channels 16kk + 8half ..
+  // +7).  Held in 32 registers, except with V block means: there the
+  // restore needs those registers, so it is rebuilt from the (L2-resident) Q
+  // codes at each batch by the hardware E4M3 convert (v_cvt_pk_f32_fp8, the
+  // OCP format of the codes), which keeps LDS free for the staged K means
+  // and the fourth ring buffer.
+  const uint8_t* q8row = Q8h + (size_t)min(qrow, S - 1) * kHeadDim + 8 * half;
+  auto load_q8 = [&](u32x2 (&w)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      w[kk] = qok ? *reinterpret_cast<const u32x2*>(q8row + 16 * kk) : u32x2{0u, 0u};
+  };
+  auto dec_q8 = [&](const u32x2& w) __attribute__((always_inline)) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    const bf16x8 r = {(__bf16)a[0], (__bf16)a[1], (__bf16)b[0], (__bf16)b[1],
+                      (__bf16)c2[0], (__bf16)c2[1], (__bf16)d[0], (__bf16)d[1]};
+    return r;
+  };
   bf16x8 qh_reg[8];
+  if (!kVBlock) {
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const uint8_t* p = Q8h + (size_t)qrow * kHeadDim + 16 * kk + 8 * half;
-    const u32x2 w = qok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint8_t* p = Q8h + (size_t)qrow * kHeadDim + 16 * kk + 8 * half;
+      const u32x2 w = qok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qh_reg[kk][e] = (__bf16)e4m3_value((w[e >> 2] >> (8 * (e & 3))) & 255u);
-    if (kVBlock) lds_qh[wave][kk][lane] = qh_reg[kk];
+      for (int e = 0; e < 8; ++e) qh_reg[kk][e] = (__bf16)e4m3_value((w[e >> 2] >> (8 * (e & 3))) & 255u);
+    }
   }
   const int nbm = kBlockMean ? nkt_all : 1;
   const float* kmh = k_mean + (size_t)bh * nbm * kHeadDim;
@@ -290,6 +307,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     f32x16 cm;
 #pragma unroll
     for (int i = 0; i < 16; ++i) cm[i] = 0.f;
+    u32x2 q8w[8];
+    if (kVBlock) load_q8(q8w);
     const float* km = kmh + (size_t)kmean_block(b0 + col) * kHeadDim;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -308,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
           lo[e] = (__bf16)(x - (float)hi[e]);
         }
       }
-      const bf16x8 qh = kVBlock ? lds_qh[wave][kk][lane] : qh_reg[kk];
+      const bf16x8 qh = kVBlock ? dec_q8(q8w[kk]) : qh_reg[kk];
       cm = mfma32x32x16_bf16(hi, qh, cm);
       cm = mfma32x32x16_bf16(lo, qh, cm);
     }
