@@ -42,21 +42,63 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_launches(fn, steps, warmup):
+def time_launches(fn, steps, warmup, detail=False):
     """Average ms per launch over `steps` launches after `warmup` ones, with
-    HIP events recorded on torch's current stream (the launch stream)."""
+    HIP events recorded on torch's current stream (the launch stream).
+
+    With `detail`, an event also follows every launch, and while the launches
+    run the host samples the graphics clock from sysfs; it then returns
+    (average ms, per-launch ms list, clock samples in MHz)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if detail else 2)]
+    marks[0].record()
+    for i in range(steps):
         fn()
-    end.record()
+        if detail:
+            marks[i + 1].record()
+    marks[-1].record()
+    clocks = []
+    path = sclk_path() if detail else None
+    while path and not marks[-1].query():
+        mhz = read_sclk(path)
+        if mhz is not None:
+            clocks.append(mhz)
+        time.sleep(0.01)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    avg = marks[0].elapsed_time(marks[-1]) / steps
+    if not detail:
+        return avg
+    return avg, [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)], clocks
+
+
+def sclk_path():
+    """The sysfs file that lists the graphics clock levels of torch's device
+    0, the current one marked with '*'; None if the driver exposes none."""
+    import glob
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    path = "/sys/bus/pci/devices/%04x:%02x:%02x.0/pp_dpm_sclk" % (
+        p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+    if os.access(path, os.R_OK):
+        return path
+    found = [f for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk") if os.access(f, os.R_OK)]
+    return found[0] if len(found) == 1 else None
+
+
+def read_sclk(path):
+    """Current graphics clock in MHz from a pp_dpm_sclk listing, or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    digits = "".join(c for c in line.split(":", 1)[1] if c.isdigit() or c == ".")
+                    return float(digits) if digits else None
+    except (OSError, IndexError, ValueError):
+        return None
+    return None
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "video_diffusion_transformer_vdit_amd", "csrc", "attn_bf16.hip")
@@ -172,8 +214,10 @@ def main():
     q, k, v = dev(qb), dev(kb), dev(vb)
     o = torch.empty_like(q)
     log("[bench] bf16 attention")
-    ms = time_launches(lambda: binding.vdit_attn_fwd(q, k, v, o=o, scale=scale), args.steps, args.warmup)
+    ms, per_launch, clocks = time_launches(lambda: binding.vdit_attn_fwd(q, k, v, o=o, scale=scale),
+                                           args.steps, args.warmup, detail=True)
     tflops = w.flop / (ms * 1e-3) / 1e12
+    sclk = float(np.median(clocks)) if clocks else None
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -201,6 +245,16 @@ def main():
             "algorithmic_flop_per_launch": w.flop,
             "algorithmic_bytes_per_launch": 4 * w.B * w.H * w.S * w.D * 2,
         },
+        "launch_ms": {"median": round(float(np.median(per_launch)), 4),
+                      "min": round(min(per_launch), 4), "max": round(max(per_launch), 4)},
+        # one exponential per (query, key) score
+        "exp2_per_s": float("%.4g" % (w.B * w.H * w.S * w.S / (ms * 1e-3))),
+        # graphics clock sampled from sysfs while the timed launches ran, and
+        # the dense bf16 peak rescaled from the 2.4 GHz nameplate to it
+        "sclk_mhz": {"median": sclk, "min": min(clocks) if clocks else None,
+                     "max": max(clocks) if clocks else None, "samples": len(clocks)},
+        "peak_at_observed_clock": round(PEAK_BF16_TFLOPS * sclk / 2400.0, 1) if sclk else None,
+        "frac_at_observed_clock": round(tflops / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4) if sclk else None,
     }
 
     # block-causal variant, one chunk per latent frame; FLOP counts only the
