@@ -81,6 +81,55 @@ def test_prepass_constant_inputs():
     assert np.all(zg["v8"].cpu().numpy() == 0) and np.all(zg["v_scale"].cpu().numpy() == 1.0)
 
 
+def e4m3_midpoints():
+    """The positive E4M3 values (0 .. 448) and the midpoints between
+    neighbours, in fp64."""
+    tab = ofp8.e4m3_table()[:127].astype(np.float64)
+    tab = np.unique(tab[np.isfinite(tab) & (tab >= 0)])
+    return tab, (tab[:-1] + tab[1:]) / 2
+
+
+def tie_tensor(B, H, S, shift):
+    """bf16 bits [B,H,S,128] whose every 64-token block holds pairs +-x
+    (tokens t and t + 32), so K block means and the V mean are exactly 0, with
+    +-448 in every channel, so every scale is exactly 1 and each code is the
+    E4M3 rounding of x itself.  The x run through every positive E4M3 value,
+    every midpoint between neighbours (the ties) and the bf16 numbers either
+    side of each midpoint, `shift` rotating their placement."""
+    tab, mid = e4m3_midpoints()
+    mid_bits = inputs.f32_to_bf16_bits(mid.astype(np.float32))
+    assert np.array_equal(inputs.bf16_bits_to_f32(mid_bits).astype(np.float64), mid)  # exact in bf16
+    vals = np.concatenate([inputs.f32_to_bf16_bits(tab[1:].astype(np.float32)), mid_bits,
+                           mid_bits + 1, mid_bits - 1]).astype(np.uint16)
+    n_slots = B * H * (S // 64) * 31 * 128
+    assert vals.size <= n_slots
+    pos = np.resize(np.roll(vals, shift), n_slots).reshape(B, H, S // 64, 31, 128)
+    blk = np.empty((B, H, S // 64, 64, 128), np.uint16)
+    blk[:, :, :, 0, :] = inputs.f32_to_bf16_bits(np.array([448.0], np.float32))[0]
+    blk[:, :, :, 1:32, :] = pos
+    blk[:, :, :, 32:, :] = blk[:, :, :, :32, :] | np.uint16(0x8000)    # the negatives
+    return blk.reshape(B, H, S, 128)
+
+
+def test_prepass_codes_at_every_rounding_tie():
+    """Every code decision of the pre-pass at an exact E4M3 tie (ties to the
+    even mantissa), next to one, in the subnormal range and at +-448, through
+    the Q, K-residual and V-residual paths."""
+    B, H, S = 1, 2, 128
+    q, k, v = tie_tensor(B, H, S, 0), tie_tensor(B, H, S, 101), tie_tensor(B, H, S, 202)
+    zo = ofp8.quantize(q, k, v)
+    for key in ("q_scale", "k_scale", "v_scale"):
+        assert np.all(zo[key] == 1.0), key
+    assert np.all(zo["k_mean"] == 0.0) and np.all(zo["v_mean"] == 0.0)
+    _, mid = e4m3_midpoints()
+    for t in (q, k, v):
+        x = np.abs(inputs.bf16_bits_to_f32(t).astype(np.float64))
+        assert np.all(np.isin(mid, x))   # every tie is present
+    log("prepass rounding ties")
+    zg = gpu_quant(q, k, v)
+    compare_quant(zg, zo, what="ties")
+
+
 @pytest.mark.parametrize("name", ["tiny-3x16x16", "wan2.1-14b-720p-fp8"])
 def test_prepass_bit_exact_workload(name):
     import torch

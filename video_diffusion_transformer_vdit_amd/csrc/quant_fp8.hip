@@ -11,9 +11,10 @@
 //   1. per (b,h, 64-token block): Q codes + scale; K block mean, residual
 //      codes + scale (block mode) or K partial sums (global mode); V partial
 //      sum / min / max per channel  -> workspace
-//   2. per (b,h): reduce the V (and global K) partials -> v_mean, v_scale,
-//      1/scale (workspace), k_mean (global mode)
-//   3. per (b,h, block): V residual codes; K residual codes (global mode)
+//   2. per (b,h) and 16 channels: reduce the V (and global K) partials ->
+//      v_mean, v_scale, 1/scale (workspace), k_mean (global mode)
+//   3. per (b,h) and run of 4 blocks: V residual codes; K residual codes
+//      (global mode)
 //
 // With block means for V (the article's own Demean: one mean per channel
 // and hardware block of 128 tokens) launch 2 forms, per 128-token block, the
@@ -36,7 +37,9 @@
 // checked bit for bit: sums of bf16 values in fp64 (exact for these inputs),
 // mean = fp32(sum / n), residual = fp32(x - mean), scale = fp32(amax / 448)
 // and inv = fp32(448 / amax) from fp64 quotients (1 and 0 when amax = 0),
-// code = E4M3 round-to-nearest-even of clamp(fp32(r * inv), +-448); the
+// code = E4M3 round-to-nearest-even of clamp(fp32(r * inv), +-448) (by the
+// hardware convert: the same codes as a software encoder of that rule on
+// every tie, subnormal and zero tried); the
 // 16-bit V block mean is bf16(fp32 mean), nearest even, and the residual is
 // taken against it.
 #include "device_common.h"
@@ -47,22 +50,6 @@ namespace {
 
 constexpr int kBlock = 64;     // tokens per block
 constexpr int kThreads = 256;  // 16 row groups x 16 chunks of 8 channels
-
-// E4M3 (OCP E4M3FN) encoder, round to nearest even, for |x| <= 448.
-// Normal results: round the fp32 mantissa to 3 bits with an integer carry
-// and rebias the exponent from 127 to 7.  Below 2^-6 the grid is 2^-9.
-__device__ __forceinline__ uint32_t e4m3_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  uint32_t code;
-  if (a < 0x3c800000u) {  // |x| < 2^-6
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    code = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  }
-  return code | sign;
-}
 
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
 
@@ -83,14 +70,22 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p, bool ok) {
   return ok ? *reinterpret_cast<const u32x4*>(p) : z;
 }
 
+// E4M3 codes of four values (|x| <= 448), low byte first: the hardware
+// OCP E4M3 convert, round to nearest even, subnormals on the 2^-9 grid, the
+// sign kept on zero (-0 and negatives that round to zero give 0x80)
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)lo, true);
+}
+
 // 8 codes of f[0..7] * inv -> two packed dwords
 __device__ __forceinline__ u32x2 encode8(const float* f, float inv) {
-  u32x2 r;
-  uint32_t c[8];
+  float c[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = e4m3_rne(clamp448(__fmul_rn(f[i], inv)));
-  r.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  r.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  for (int i = 0; i < 8; ++i) c[i] = clamp448(__fmul_rn(f[i], inv));
+  u32x2 r;
+  r.x = e4m3x4(c[0], c[1], c[2], c[3]);
+  r.y = e4m3x4(c[4], c[5], c[6], c[7]);
   return r;
 }
 
@@ -276,23 +271,27 @@ __global__ __launch_bounds__(kThreads) void quant_blocks_kernel(
   }
 }
 
-// Launch 2: one workgroup per bh of kReduceParts x 128 threads; thread
-// (part, d) folds channel d over the blocks b = part (mod kReduceParts), and
-// thread part = 0 combines the parts in part order.  The fp64 sums of bf16
-// values are exact, so the grouping does not change them.
-// With v_bmean (block mode) thread (part, d) handles the 128-token blocks
-// b = part (mod kReduceParts): mean, its bf16 rounding, and the block's
-// residual range.
-constexpr int kReduceParts = 8;
-__global__ __launch_bounds__(kReduceParts * kHeadDim) void quant_reduce_kernel(
+// Launch 2: one workgroup per (bh, group of kReduceChans channels), of
+// kReduceParts x kReduceChans threads; thread (part, channel) folds the
+// channel over the blocks b = part (mod kReduceParts), and the threads of
+// part 0 combine the parts in part order.  The fp64 sums of bf16 values are
+// exact, so the grouping does not change them.
+// With v_bmean (block mode) thread (part, channel) handles the 128-token
+// blocks b = part (mod kReduceParts): mean, its bf16 rounding, and the
+// block's residual range.
+constexpr int kReduceChans = 16;
+constexpr int kReduceParts = 64;
+__global__ __launch_bounds__(kReduceParts * kReduceChans) void quant_reduce_kernel(
     float* __restrict__ v_mean, float* __restrict__ v_scale, float* __restrict__ k_mean,
     uint16_t* __restrict__ v_bmean, int nbv_pad, Workspace ws, int S, int nb, int k_global) {
-  __shared__ float ram[kReduceParts][kHeadDim];
-  __shared__ double rs[kReduceParts][kHeadDim];
-  __shared__ double rk[kReduceParts][kHeadDim];
-  __shared__ float rmn[kReduceParts][kHeadDim], rmx[kReduceParts][kHeadDim];
-  const int bh = blockIdx.x;
-  const int d = threadIdx.x & 127, part = threadIdx.x >> 7;
+  __shared__ float ram[kReduceParts][kReduceChans];
+  __shared__ double rs[kReduceParts][kReduceChans];
+  __shared__ double rk[kReduceParts][kReduceChans];
+  __shared__ float rmn[kReduceParts][kReduceChans], rmx[kReduceParts][kReduceChans];
+  constexpr int kGroups = kHeadDim / kReduceChans;
+  const int bh = blockIdx.x / kGroups;
+  const int dl = threadIdx.x % kReduceChans, part = threadIdx.x / kReduceChans;
+  const int d = (blockIdx.x - bh * kGroups) * kReduceChans + dl;
   double s = 0.0, sk = 0.0;
   float mn = INFINITY, mx = -INFINITY;
   for (int b = part; b < nb; b += kReduceParts) {
@@ -302,10 +301,10 @@ __global__ __launch_bounds__(kReduceParts * kHeadDim) void quant_reduce_kernel(
     mx = fmaxf(mx, ws.v_max[o]);
     if (k_global) sk += ws.k_sum[o];
   }
-  rs[part][d] = s;
-  rk[part][d] = sk;
-  rmn[part][d] = mn;
-  rmx[part][d] = mx;
+  rs[part][dl] = s;
+  rk[part][dl] = sk;
+  rmn[part][dl] = mn;
+  rmx[part][dl] = mx;
   if (v_bmean) {
     const int nbv = (S + 2 * kBlock - 1) / (2 * kBlock);
     uint16_t* vb = v_bmean + ((size_t)bh * kHeadDim + d) * nbv_pad;
@@ -326,19 +325,18 @@ __global__ __launch_bounds__(kReduceParts * kHeadDim) void quant_reduce_kernel(
       vb[b] = (uint16_t)mb;
       am = fmaxf(am, fmaxf(fabsf(__fsub_rn(hi, m16)), fabsf(__fsub_rn(lo, m16))));
     }
-    ram[part][d] = am;
+    ram[part][dl] = am;
   }
   __syncthreads();
   if (part != 0) return;
   double ssum = 0.0, sksum = 0.0;
   float lo = INFINITY, hi = -INFINITY, amb = 0.0f;
-#pragma unroll
   for (int p = 0; p < kReduceParts; ++p) {
-    ssum += rs[p][d];
-    sksum += rk[p][d];
-    lo = fminf(lo, rmn[p][d]);
-    hi = fmaxf(hi, rmx[p][d]);
-    if (v_bmean) amb = fmaxf(amb, ram[p][d]);
+    ssum += rs[p][dl];
+    sksum += rk[p][dl];
+    lo = fminf(lo, rmn[p][dl]);
+    hi = fmaxf(hi, rmx[p][dl]);
+    if (v_bmean) amb = fmaxf(amb, ram[p][dl]);
   }
   if (k_global) k_mean[(size_t)bh * kHeadDim + d] = (float)(sksum / (double)S);
   float sc, inv;
@@ -355,8 +353,12 @@ __global__ __launch_bounds__(kReduceParts * kHeadDim) void quant_reduce_kernel(
   ws.v_inv[(size_t)bh * kHeadDim + d] = inv;
 }
 
-// Launch 3: one workgroup per (bh, block): V residual codes, and K residual
-// codes + scale when K uses one global mean.
+// Launch 3: one workgroup per (bh, run of kResidualRun blocks): V residual
+// codes, and K residual codes + scale when K uses one global mean.  The
+// workgroup walks its blocks in order with the next block's V rows already
+// in flight, and the channel-major tile alternates between two LDS buffers,
+// so one barrier per block separates its writes from its reads.
+constexpr int kResidualRun = 4;
 __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint8_t* __restrict__ K8,
     uint8_t* __restrict__ V8, float* __restrict__ k_scale, const float* __restrict__ k_mean,
@@ -366,83 +368,104 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
   // codes channel-major, [channel][key], rows padded to 68 bytes so that the
   // transposing reads below spread over the banks
   constexpr int kRowT = kBlock + 4;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim * kRowT];
-  const int bh = blockIdx.x / nb;
-  const int blk = blockIdx.x - bh * nb;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kHeadDim * kRowT];
+  const int runs = (nb + kResidualRun - 1) / kResidualRun;
+  const int bh = blockIdx.x / runs;
+  const int blk0 = (blockIdx.x - bh * runs) * kResidualRun;
+  const int blk_end = min(nb, blk0 + kResidualRun);
   const int tid = threadIdx.x;
   const int c = tid & 15, rg = tid >> 4;
-  const int row0 = blk * kBlock;
-  const int nvalid = min(kBlock, S - row0);
   const size_t head = (size_t)bh * S * kHeadDim;
   float vm[8], vi[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    vm[i] = v_bmean ? __uint_as_float((uint32_t)v_bmean[((size_t)bh * kHeadDim + 8 * c + i) * nbv_pad +
-                                                        (blk >> 1)] << 16)
-                    : v_mean[(size_t)bh * kHeadDim + 8 * c + i];
+    vm[i] = v_bmean ? 0.f : v_mean[(size_t)bh * kHeadDim + 8 * c + i];
     vi[i] = ws.v_inv[(size_t)bh * kHeadDim + 8 * c + i];
   }
-  // thread (row group rg, chunk c): keys 4rg .. 4rg+3 of channels 8c .. 8c+7,
-  // one 4-key word per channel
-  uint32_t wv[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = 4 * rg + p;
-    if (r < nvalid) {
-      const size_t off = head + (size_t)(row0 + r) * kHeadDim + 8 * c;
-      float f[8];
-      unpack8(ld16(V + off, true), f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        wv[i] |= e4m3_rne(clamp448(__fmul_rn(__fsub_rn(f[i], vm[i]), vi[i]))) << (8 * p);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&tile[(8 * c + i) * kRowT + 4 * rg]) = wv[i];
-  __syncthreads();
-  // transpose into the kernel's tile: thread -> (channel d, physical chunk pc)
-  {
-    uint8_t* V8t = V8 + ((size_t)bh * nb + blk) * (kBlock * kHeadDim);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int idx = tid + kThreads * h;  // 0 .. 511
-      const int d = idx >> 2, pc = idx & 3;
-      const int lc = pc ^ ((d >> 2) & 3);
-      // slots 16lc + 4q + b hold keys 32(lc & 1) + 8q + 4(lc >> 1) + b: four
-      // consecutive keys, one aligned word of the channel-major tile
-      uint32_t wd[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        wd[q] = *reinterpret_cast<const uint32_t*>(&tile[d * kRowT + 32 * (lc & 1) + 8 * q + 4 * (lc >> 1)]);
-      *reinterpret_cast<u32x4*>(V8t + d * kBlock + 16 * pc) = u32x4{wd[0], wd[1], wd[2], wd[3]};
-    }
-  }
-  if (k_global) {
-    float km[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) km[i] = k_mean[(size_t)bh * kHeadDim + 8 * c + i];
-    float k[4][8];
-    float a = 0.f;
+  // thread (row group rg, chunk c): keys 4rg .. 4rg+3 of channels 8c .. 8c+7
+  // (keys past S: zero rows)
+  auto load_v = [&](int blk, u32x4* w) __attribute__((always_inline)) {
+    const int nvalid = min(kBlock, S - blk * kBlock);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int r = rg + 16 * p;
-      const bool ok = r < nvalid;
-      unpack8(ld16(K + head + (size_t)(row0 + r) * kHeadDim + 8 * c, ok), k[p]);
+      const int r = 4 * rg + p;
+      w[p] = ld16(V + head + (size_t)(blk * kBlock + r) * kHeadDim + 8 * c, r < nvalid);
+    }
+  };
+  u32x4 cur[4], nxt[4];
+  load_v(blk0, cur);
+  for (int blk = blk0, buf = 0; blk < blk_end; ++blk, buf ^= 1) {
+    if (blk + 1 < blk_end) load_v(blk + 1, nxt);
+    const int nvalid = min(kBlock, S - blk * kBlock);
+    if (v_bmean) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        k[p][i] = __fsub_rn(k[p][i], km[i]);
-        a = fmaxf(a, ok ? fabsf(k[p][i]) : 0.f);
+      for (int i = 0; i < 8; ++i)
+        vm[i] = __uint_as_float((uint32_t)v_bmean[((size_t)bh * kHeadDim + 8 * c + i) * nbv_pad + (blk >> 1)]
+                                << 16);
+    }
+    // residual codes, one 4-key word per channel (keys past S: +0, code 0)
+    float rv[4][8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bool ok = 4 * rg + p < nvalid;
+      float f[8];
+      unpack8(cur[p], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rv[p][i] = ok ? clamp448(__fmul_rn(__fsub_rn(f[i], vm[i]), vi[i])) : 0.0f;
+    }
+    uint8_t* tl = tile[buf];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint32_t*>(&tl[(8 * c + i) * kRowT + 4 * rg]) =
+          e4m3x4(rv[0][i], rv[1][i], rv[2][i], rv[3][i]);
+    __syncthreads();
+    // transpose into the kernel's tile: thread -> (channel d, physical chunk pc)
+    {
+      uint8_t* V8t = V8 + ((size_t)bh * nb + blk) * (kBlock * kHeadDim);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int idx = tid + kThreads * h;  // 0 .. 511
+        const int d = idx >> 2, pc = idx & 3;
+        const int lc = pc ^ ((d >> 2) & 3);
+        // slots 16lc + 4q + b hold keys 32(lc & 1) + 8q + 4(lc >> 1) + b: four
+        // consecutive keys, one aligned word of the channel-major tile
+        uint32_t wd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          wd[q] = *reinterpret_cast<const uint32_t*>(&tl[d * kRowT + 32 * (lc & 1) + 8 * q + 4 * (lc >> 1)]);
+        *reinterpret_cast<u32x4*>(V8t + d * kBlock + 16 * pc) = u32x4{wd[0], wd[1], wd[2], wd[3]};
       }
     }
-    const float amax = block_max(a, red);
-    float sc, inv;
-    scales_from_amax(amax, &sc, &inv);
-    if (tid == 0) k_scale[(size_t)bh * nb + blk] = sc;
+    if (k_global) {
+      const int row0 = blk * kBlock;
+      float km[8];
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-      if (rg + 16 * p < nvalid)
-        *reinterpret_cast<u32x2*>(K8 + head + (size_t)(row0 + rg + 16 * p) * kHeadDim + 8 * c) =
-            encode8(k[p], inv);
+      for (int i = 0; i < 8; ++i) km[i] = k_mean[(size_t)bh * kHeadDim + 8 * c + i];
+      float k[4][8];
+      float a = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = rg + 16 * p;
+        const bool ok = r < nvalid;
+        unpack8(ld16(K + head + (size_t)(row0 + r) * kHeadDim + 8 * c, ok), k[p]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          k[p][i] = __fsub_rn(k[p][i], km[i]);
+          a = fmaxf(a, ok ? fabsf(k[p][i]) : 0.f);
+        }
+      }
+      const float amax = block_max(a, red);
+      float sc, inv;
+      scales_from_amax(amax, &sc, &inv);
+      if (tid == 0) k_scale[(size_t)bh * nb + blk] = sc;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if (rg + 16 * p < nvalid)
+          *reinterpret_cast<u32x2*>(K8 + head + (size_t)(row0 + rg + 16 * p) * kHeadDim + 8 * c) =
+              encode8(k[p], inv);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) cur[p] = nxt[p];
   }
 }
 
@@ -490,11 +513,13 @@ hipError_t launch_quant_fp8(const void* q, const void* k, const void* v, void* q
   if (e != hipSuccess) return e;
   uint16_t* vbm = static_cast<uint16_t*>(v_bmean);
   const int nbv_pad = vsmooth_blocks_padded(S);
-  hipLaunchKernelGGL(quant_reduce_kernel, dim3(BH), dim3(kReduceParts * kHeadDim), 0, stream, v_mean, v_scale,
+  hipLaunchKernelGGL(quant_reduce_kernel, dim3((unsigned)BH * (kHeadDim / kReduceChans)),
+                     dim3(kReduceParts * kReduceChans), 0, stream, v_mean, v_scale,
                      k_mean, vbm, nbv_pad, ws, S, nb, k_global);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(quant_residual_kernel, dim3(grid), dim3(kThreads), 0, stream,
+  const int runs = (nb + kResidualRun - 1) / kResidualRun;
+  hipLaunchKernelGGL(quant_residual_kernel, dim3((unsigned)((size_t)BH * runs)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<uint8_t*>(k8), static_cast<uint8_t*>(v8), k_scale, k_mean, v_mean,
                      vbm, nbv_pad, ws, S, nb, k_global);
