@@ -397,7 +397,8 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
   for (int blk = blk0, buf = 0; blk < blk_end; ++blk, buf ^= 1) {
     if (blk + 1 < blk_end) load_v(blk + 1, nxt);
     const int nvalid = min(kBlock, S - blk * kBlock);
-    if (v_bmean) {
+    // (a V block mean spans two 64-token blocks)
+    if (v_bmean && ((blk & 1) == 0 || blk == blk0)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         vm[i] = __uint_as_float((uint32_t)v_bmean[((size_t)bh * kHeadDim + 8 * c + i) * nbv_pad + (blk >> 1)]
