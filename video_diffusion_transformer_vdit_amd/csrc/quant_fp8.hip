@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void quant_residual_kernel(
       w[p] = ld16(V + head + (size_t)(blk * kBlock + r) * kHeadDim + 8 * c, r < nvalid);
     }
   };
-  u32x4 cur[4], nxt[4];
+  u32x4 cur[4], nxt[4] = {};
   load_v(blk0, cur);
   for (int blk = blk0, buf = 0; blk < blk_end; ++blk, buf ^= 1) {
     if (blk + 1 < blk_end) load_v(blk + 1, nxt);
