@@ -63,7 +63,7 @@ def test_separated_points_bit_exact():
             np.testing.assert_array_equal(cent[b, h], oa.widen_bf16(pts[b, h]).astype(np.float32))
 
 
-@pytest.mark.parametrize("S,k,rounds", [(1, 1, 2), (130, 2, 0), (5000, 40, 4), (9000, 71, 2)])
+@pytest.mark.parametrize("S,k,rounds", [(1, 1, 2), (130, 2, 0), (5000, 40, 4), (9000, 71, 2), (8192, 4096, 1)])
 def test_general_data_properties(S, k, rounds):
     B, H = 1, 2
     v = clustered_bits(B, H, S, max(1, k // 2), seed=S + k)

@@ -210,54 +210,128 @@ __global__ __launch_bounds__(256) void group_hist_kernel(const int* __restrict__
   for (int c = threadIdx.x; c < k; c += 256) h[c] = cnt_s[c];
 }
 
-// grid BH, 256 threads: cluster offsets and per-chunk placement bases
+// grid BH, 256 threads: cluster offsets and per-chunk placement bases.
+// Integer sums, so the grouping of the additions does not matter.
 __global__ __launch_bounds__(256) void group_scan_kernel(GroupWs ws, int k, int nchunk) {
   extern __shared__ int tot_s[];
+  __shared__ int part_s[256];
   const int bh = blockIdx.x;
   int* h = ws.hist + (size_t)bh * nchunk * k;
+  // cluster totals over the chunks, eight loads in flight
   for (int c = threadIdx.x; c < k; c += 256) {
-    int s = 0;
-    for (int ch = 0; ch < nchunk; ++ch) s += h[(size_t)ch * k + c];
+    int s = 0, ch = 0;
+    for (; ch + 8 <= nchunk; ch += 8) {
+      int x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = h[(size_t)(ch + u) * k + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += x[u];
+    }
+    for (; ch < nchunk; ++ch) s += h[(size_t)ch * k + c];
     tot_s[c] = s;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int c = 0; c < k; ++c) {
-      const int n = tot_s[c];
-      ws.cnt[(size_t)bh * k + c] = n;
-      ws.seg[(size_t)bh * k + c] = run;
-      tot_s[c] = run;
-      run += n;
-    }
+  // exclusive prefix over the clusters: thread t owns a run of `per`
+  // consecutive clusters; the runs' sums are scanned in LDS
+  const int per = (k + 255) / 256;
+  const int c0 = min(k, (int)threadIdx.x * per), c1 = min(k, c0 + per);
+  int run = 0;
+  for (int c = c0; c < c1; ++c) run += tot_s[c];
+  part_s[threadIdx.x] = run;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = threadIdx.x >= off ? part_s[threadIdx.x - off] : 0;
+    __syncthreads();
+    part_s[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int base = threadIdx.x > 0 ? part_s[threadIdx.x - 1] : 0;
+  for (int c = c0; c < c1; ++c) {
+    const int n = tot_s[c];
+    ws.cnt[(size_t)bh * k + c] = n;
+    ws.seg[(size_t)bh * k + c] = base;
+    tot_s[c] = base;
+    base += n;
   }
   __syncthreads();
+  // each chunk's first position in each cluster (chunks in token order)
   for (int c = threadIdx.x; c < k; c += 256) {
-    int base = tot_s[c];
-    for (int ch = 0; ch < nchunk; ++ch) {
+    int b = tot_s[c], ch = 0;
+    for (; ch + 8 <= nchunk; ch += 8) {
+      int x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = h[(size_t)(ch + u) * k + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        h[(size_t)(ch + u) * k + c] = b;
+        b += x[u];
+      }
+    }
+    for (; ch < nchunk; ++ch) {
       const int n = h[(size_t)ch * k + c];
-      h[(size_t)ch * k + c] = base;
-      base += n;
+      h[(size_t)ch * k + c] = b;
+      b += n;
     }
   }
 }
 
 // grid (BH * nchunk), 256 threads: the chunk's tokens go to their cluster's
-// next positions in token order (one thread walks the chunk)
+// next positions in token order.  Wave w takes tokens 256w .. 256w+255 of
+// the chunk; per-wave label counts give each wave its offset in each cluster
+// within the chunk, and within a wave 64 tokens at a time are ranked among
+// the earlier lanes with the same label, so the placement is stable.  The
+// four waves' counts, then offsets (at most 1,024), are 16-bit halves of two
+// words per cluster.
 __global__ __launch_bounds__(256) void group_place_kernel(const int* __restrict__ labels,
                                                           int* __restrict__ perm, GroupWs ws, int S,
                                                           int k, int nchunk) {
-  extern __shared__ int base_s[];  // [k] bases, then [kChunk] labels
-  int* lab_s = base_s + k;
+  // [k] chunk bases, [2][k] packed per-wave counts / offsets, [kChunk] labels
+  extern __shared__ int base_s[];
+  uint32_t* pair_s = reinterpret_cast<uint32_t*>(base_s + k);
+  uint16_t* off_s = reinterpret_cast<uint16_t*>(pair_s);
+  int* lab_s = base_s + 3 * k;
   const int bh = blockIdx.x / nchunk, ch = blockIdx.x - bh * nchunk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int* h = ws.hist + ((size_t)bh * nchunk + ch) * k;
-  for (int c = threadIdx.x; c < k; c += 256) base_s[c] = h[c];
+  for (int c = threadIdx.x; c < k; c += 256) {
+    base_s[c] = h[c];
+    pair_s[c] = 0u;
+    pair_s[k + c] = 0u;
+  }
   const int t0 = ch * kChunk, n = min(S - t0, kChunk);
-  for (int t = threadIdx.x; t < n; t += 256) lab_s[t] = labels[(size_t)bh * S + t0 + t];
+  for (int t = threadIdx.x; t < kChunk; t += 256) lab_s[t] = t < n ? labels[(size_t)bh * S + t0 + t] : -1;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int* p = perm + (size_t)bh * S;
-    for (int t = 0; t < n; ++t) p[base_s[lab_s[t]]++] = t0 + t;
+  // wave w counts into half (w & 1) of word (w >> 1) * k + label
+  for (int i = 0; i < kChunk / 256; ++i) {
+    const int lab = lab_s[256 * wave + 64 * i + lane];
+    if (lab >= 0) atomicAdd(&pair_s[(wave >> 1) * k + lab], 1u << (16 * (wave & 1)));
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < k; c += 256) {
+    const uint32_t a = pair_s[c], b = pair_s[k + c];
+    const uint32_t o1 = a & 0xffffu, o2 = o1 + (a >> 16), o3 = o2 + (b & 0xffffu);
+    pair_s[c] = o1 << 16;
+    pair_s[k + c] = o2 | (o3 << 16);
+  }
+  __syncthreads();
+  uint16_t* wo = off_s + 2 * (wave >> 1) * k + (wave & 1);  // wave's offset of label c: wo[2c]
+  int* p = perm + (size_t)bh * S;
+  for (int i = 0; i < kChunk / 256; ++i) {
+    const int t = 256 * wave + 64 * i + lane;
+    const int lab = lab_s[t];
+    int rank = 0, total = 0;
+#pragma unroll 8
+    for (int j = 0; j < 64; ++j) {
+      const int eq = __builtin_amdgcn_readlane(lab, j) == lab;
+      total += eq;
+      rank += (j < lane) & eq;
+    }
+    if (lab >= 0) {
+      const int o = wo[2 * lab];
+      p[base_s[lab] + o + rank] = t0 + t;
+      // the first lane of each label moves the wave's offset past the group
+      if (rank == 0) wo[2 * lab] = (uint16_t)(o + total);
+    }
   }
 }
 
@@ -347,7 +421,7 @@ hipError_t launch_vsmooth_group(const void* v, int* perm, int* labels, float* ce
                        S, k, nchunk);
     hipLaunchKernelGGL(group_scan_kernel, dim3(BH), dim3(256), lds_k, stream, ws, k, nchunk);
     hipLaunchKernelGGL(group_place_kernel, dim3(BH * nchunk), dim3(256),
-                       lds_k + kChunk * sizeof(int), stream, labels, perm, ws, S, k, nchunk);
+                       3 * lds_k + kChunk * sizeof(int), stream, labels, perm, ws, S, k, nchunk);
     if (r < rounds)
       hipLaunchKernelGGL(group_update_kernel, dim3(BH * k), dim3(128), 0, stream, V, perm,
                          centroids, ws, S, k, kpad);
