@@ -79,16 +79,19 @@ __global__ __launch_bounds__(128) void group_init_kernel(const uint16_t* __restr
 
 // grid (BH * ceil(S / 512)), 512 threads: wave w scores tokens 64w .. 64w+63
 // of the workgroup's 512 (two 32-token column blocks) against all centroids,
-// 32 at a time.  Each chunk of centroids (bf16 high and residual rows, 16 KB)
-// is staged once in LDS for the 8 waves, double-buffered: the next chunk is
-// fetched into registers while the current one is multiplied.  LDS rows
-// are [centroid][high | residual][16 chunks of 16 B], chunks XOR-swizzled by
-// centroid & 15 so the 16 lanes the LDS serves together hit 16 bank groups.
+// 32 at a time.  Each chunk of centroids (bf16 high and residual rows, 16 KB,
+// and their 32 squared norms) goes from global memory straight into LDS
+// (global_load_lds_dwordx4), once for the 8 waves, into a three-deep ring
+// filled two chunks ahead; one barrier per chunk.  LDS rows are
+// [centroid][high | residual][16 chunks of 16 B], chunks XOR-swizzled by
+// centroid & 15 so the 16 lanes the LDS serves together hit 16 bank groups
+// (the DMA's source addresses apply the permutation).
 constexpr int kAssignTokens = 64 * kAssignWaves;
 __global__ __launch_bounds__(64 * kAssignWaves) void group_assign_kernel(
     const uint16_t* __restrict__ V, int* __restrict__ labels, GroupWs ws, int S, int k, int kpad,
     int ntiles) {
-  __shared__ __attribute__((aligned(16))) char lds_a[2][32 * 2 * 256];
+  __shared__ __attribute__((aligned(1024))) char lds_a[3][32 * 2 * 256];
+  __shared__ __attribute__((aligned(16))) float lds_m2[3][32];
   const int bh = blockIdx.x / ntiles, tile = blockIdx.x - bh * ntiles;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
@@ -104,40 +107,48 @@ __global__ __launch_bounds__(64 * kAssignWaves) void group_assign_kernel(
   }
   const uint16_t* muh = ws.muh + (size_t)bh * kpad * 2 * kHeadDim;
   const float* m2 = ws.m2 + (size_t)bh * kpad;
-  // staging: thread t moves 16-byte items t and t + 512 of a chunk; with it
-  // come the lane's |mu|^2 values of the chunk, centroids c0 + 8ii + 4half +
-  // 0..3 (in bounds: the arrays are padded to a multiple of 32 centroids;
-  // the padding is never selected)
-  u32x4 st[2];
-  f32x4 m2n[4];
-  auto fetch = [&](int c0) __attribute__((always_inline)) {
+  // DMA: wave w fills LDS slots L = 128w + 64u + lane (u = 0, 1) of 16 B,
+  // slot L = (2 centroid + part) * 16 + (chunk ^ (centroid & 15)); the
+  // arrays are padded to a multiple of 32 centroids, so every chunk is in
+  // bounds (the padding is never selected).  Lanes 0-7 of every wave also
+  // bring the chunk's 32 norms (the same bytes from each wave).
+  uint32_t voff[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = threadIdx.x + 512 * u, r = i >> 5, hl = (i >> 4) & 1, q = i & 15;
-      st[u] = *reinterpret_cast<const u32x4*>(muh + ((size_t)(c0 + r) * 2 + hl) * kHeadDim + 8 * q);
-    }
+  for (int u = 0; u < 2; ++u) {
+    const int L = 128 * wave + 64 * u + lane;
+    voff[u] = (uint32_t)((L >> 4) * 256 + 16 * ((L & 15) ^ ((L >> 5) & 15)));
+  }
+  const uint32_t a_base =
+      __builtin_amdgcn_readfirstlane(lds_addr(&lds_a[0][0]) + (uint32_t)wave * 2048);
+  const uint32_t m_base = lds_addr(&lds_m2[0][0]);
+  auto issue = [&](int c0, int b) __attribute__((always_inline)) {
+    const char* src = reinterpret_cast<const char*>(muh + (size_t)c0 * 2 * kHeadDim);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) m2n[ii] = *reinterpret_cast<const f32x4*>(m2 + c0 + 8 * ii + 4 * half);
+    for (int u = 0; u < 2; ++u) dma16(src, voff[u], a_base + (uint32_t)b * (32 * 2 * 256) + u * 1024);
+    if (lane < 8) dma16(reinterpret_cast<const char*>(m2 + c0), 16u * lane, m_base + (uint32_t)b * 128);
   };
-  auto stage = [&](int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = threadIdx.x + 512 * u, r = i >> 5, hl = (i >> 4) & 1, q = i & 15;
-      *reinterpret_cast<u32x4*>(&lds_a[b][((r * 2 + hl) * 16 + (q ^ (r & 15))) * 16]) = st[u];
-    }
-  };
+  const int nch = (k + 31) / 32;
   float best[2] = {INFINITY, INFINITY};
   int best_c[2] = {0x7fffffff, 0x7fffffff};
-  fetch(0);
-  stage(0);
+  // prologue: chunks 0 and 1 in flight; wait for chunk 0 (three loads per
+  // wave per chunk)
+  issue(0, 0);
+  if (nch > 1) {
+    issue(32, 1);
+    __builtin_amdgcn_s_waitcnt(0x0f73);  // vmcnt(3)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  }
+  asm volatile("" ::: "memory");
   __syncthreads();
-  int b = 0;
-  for (int c0 = 0; c0 < k; c0 += 32) {
-    const bool more = c0 + 32 < k;
+  for (int i = 0; i < nch; ++i) {
+    const int c0 = 32 * i, b = i % 3;
+    // buffer (i + 2) % 3 held chunk i - 1, which every wave finished before
+    // the last barrier
+    if (i + 2 < nch) issue(c0 + 64, (i + 2) % 3);
     f32x4 m2c[4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) m2c[ii] = m2n[ii];
-    if (more) fetch(c0 + 32);
+    for (int ii = 0; ii < 4; ++ii) m2c[ii] = *reinterpret_cast<const f32x4*>(&lds_m2[b][8 * ii + 4 * half]);
     // A operand: centroid c0 + col, logical chunk 2kk + half of each part
     bf16x8 ah[8], al[8];
 #pragma unroll
@@ -150,37 +161,41 @@ __global__ __launch_bounds__(64 * kAssignWaves) void group_assign_kernel(
     for (int j = 0; j < 2; ++j) {
       f32x16 acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int q = 0; q < 16; ++q) acc[q] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         acc = mfma32x32x16_bf16(ah[kk], vb[j][kk], acc);
         acc = mfma32x32x16_bf16(al[kk], vb[j][kk], acc);
       }
-      // lane holds centroids c0 + 8(i/4) + 4half + i%4 of its token, in
+      // lane holds centroids c0 + 8(q/4) + 4half + q%4 of its token, in
       // increasing order: a strict < keeps the lowest index on ties
       if (c0 + 32 <= k) {  // a full chunk: every centroid is real
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float d = fmaf(-2.0f, acc[i], m2c[i >> 2][i & 3]);
+        for (int q = 0; q < 16; ++q) {
+          const float d = fmaf(-2.0f, acc[q], m2c[q >> 2][q & 3]);
           const bool take = d < best[j];
           best[j] = take ? d : best[j];
-          best_c[j] = take ? c0 + 8 * (i >> 2) + 4 * half + (i & 3) : best_c[j];
+          best_c[j] = take ? c0 + 8 * (q >> 2) + 4 * half + (q & 3) : best_c[j];
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = c0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const float d = fmaf(-2.0f, acc[i], m2c[i >> 2][i & 3]);
+        for (int q = 0; q < 16; ++q) {
+          const int c = c0 + 8 * (q >> 2) + 4 * half + (q & 3);
+          const float d = fmaf(-2.0f, acc[q], m2c[q >> 2][q & 3]);
           const bool take = (c < k) & (d < best[j]);
           best[j] = take ? d : best[j];
           best_c[j] = take ? c : best_c[j];
         }
       }
     }
-    if (more) {
-      stage(b ^ 1);  // the other buffer was last read before the previous barrier
+    if (i + 1 < nch) {
+      // chunk i + 1 landed (only chunk i + 2's loads may still be in flight)
+      if (i + 2 < nch)
+        __builtin_amdgcn_s_waitcnt(0x0f73);  // vmcnt(3)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      asm volatile("" ::: "memory");
       __syncthreads();
-      b ^= 1;
     }
   }
   // the other half of the wave holds the interleaved rows for the same token
