@@ -350,32 +350,56 @@ __global__ __launch_bounds__(256) void group_place_kernel(const int* __restrict_
   }
 }
 
-// grid (BH * k), 128 threads: new centroid = mean of the cluster's tokens
-// (token order); an empty cluster keeps its centroid
+// grid (BH * k), 128 threads: new centroid = mean of the cluster's tokens;
+// an empty cluster keeps its centroid.  Thread (g, c) = (tid / 16, tid % 16)
+// sums channels 8c .. 8c+7 (one 16-byte load per token) over the members
+// g, g + 8, g + 16, ... in order, four loads in flight; the eight partial
+// sums are then added in g order, so the result is deterministic.
 __global__ __launch_bounds__(128) void group_update_kernel(const uint16_t* __restrict__ V,
                                                            const int* __restrict__ perm,
                                                            float* __restrict__ cent, GroupWs ws,
                                                            int S, int k, int kpad) {
   __shared__ float red[2];
+  __shared__ float part[8][kHeadDim];
   const int bh = blockIdx.x / k, c = blockIdx.x - bh * k;
   const int n = ws.cnt[(size_t)bh * k + c], s0 = ws.seg[(size_t)bh * k + c];
   const int d = threadIdx.x;
   float mu = cent[((size_t)bh * k + c) * kHeadDim + d];
   if (n > 0) {
+    const int g = threadIdx.x >> 4, c8 = 8 * (threadIdx.x & 15);
     const int* p = perm + (size_t)bh * S + s0;
-    const uint16_t* vh = V + (size_t)bh * S * kHeadDim + d;
-    float sum = 0.f;
-    int j = 0;
-    // eight independent loads in flight, added in token order
-    for (; j + 8 <= n; j += 8) {
-      float x[8];
+    const uint16_t* vh = V + (size_t)bh * S * kHeadDim + c8;
+    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int j = g;
+    for (; j + 24 < n; j += 32) {
+      u32x4 x[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = bf16_value(vh[(size_t)p[j + u] * kHeadDim]);
+      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const u32x4*>(vh + (size_t)p[j + 8 * u] * kHeadDim);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += x[u];
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum[2 * e] += __uint_as_float(x[u][e] << 16);
+          sum[2 * e + 1] += __uint_as_float(x[u][e] & 0xffff0000u);
+        }
     }
-    for (; j < n; ++j) sum += bf16_value(vh[(size_t)p[j] * kHeadDim]);
-    mu = sum / (float)n;
+    for (; j < n; j += 8) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(vh + (size_t)p[j] * kHeadDim);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sum[2 * e] += __uint_as_float(x[e] << 16);
+        sum[2 * e + 1] += __uint_as_float(x[e] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[g][c8 + e] = sum[e];
+  }
+  __syncthreads();
+  if (n > 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) t += part[q][d];
+    mu = t / (float)n;
   }
   store_centroid(mu, cent, ws, bh, c, k, kpad, red);
 }
