@@ -31,9 +31,11 @@ Demean, ``v_mean="block"``) by the per-channel mean of each 128-token block
 scale of the residual over the sequence; P is quantised as E4M3(448 * 2^(t -
 M)) where t is the log2-domain score and M the integer ceiling of the row
 maximum of t; the row sum is the sum of the quantised weights (so the
-weights of a row sum to one and the mean restore is exact); ExpCast rounds 8
-(t - M) + 8 log2(448) + 55.65 to the nearest integer, ties to even, clamped
-to [0, 255].
+weights of a row sum to one and the mean restore is exact); ExpCast takes the
+byte position z = 8 (t - M) + 8 log2(448) + 55.65 and rounds the value the
+byte map gives to z (exponent floor(z/8) - 7, mantissa 1 + (z mod 8)/8) to
+E4M3: in the normal range that is round-half-even(z) itself, below it the
+nearest subnormal code (the pages leave the underflow open).
 
 Precision of the integer-valued decisions (codes): the pre-pass takes them
 in the precision the kernel takes them in, so the codes can be compared bit
@@ -226,23 +228,48 @@ def quantize(q, k, v, block: int = 64, k_mean: str = "block", v_mean: str = "glo
 # v, read as an integer, is about 8 log2(v) + 56; the article writes the byte
 # of a weight directly from its log-domain score with one multiply-add and a
 # centring constant beta = -0.35.  Here the weight is 448 p with log2 p =
-# t - M, so the byte is round-to-nearest-even of 8 (t - M) + 8 log2(448) + 56
-# - 0.35, clamped to the byte range (t <= M keeps it <= 126, the code of 448).
+# t - M, so its byte position is z = 8 (t - M) + 8 log2(448) + 56 - 0.35
+# (t <= M keeps z <= 126.1, below 126.5: at most the code of 448).
 EXPCAST_BETA = -0.35
 EXPCAST_OFFSET = 8.0 * math.log2(E4M3_MAX) + 56.0 + EXPCAST_BETA
 
 
+def byte_map_value(z) -> np.ndarray:
+    """The value the E4M3 byte map gives to a real byte position z.
+
+    A normal E4M3 byte read as an integer is 8 e + m for the value
+    2^(e - 7) (1 + m / 8) (exponent field e, mantissa field m), which is why
+    the byte is close to 8 log2(v) + 56 (VC-Attention article, section 03).
+    The same rule for every real z: 2^(floor(z / 8) - 7) (1 + (z mod 8) / 8);
+    -inf gives 0.  It is exact at the bytes 8 .. 126 and commutes with powers
+    of two: byte_map_value(z + 8 k) = 2^k byte_map_value(z)."""
+    z = np.asarray(z, np.float64)
+    with np.errstate(invalid="ignore"):
+        e = np.floor(z / 8.0)
+        f = z / 8.0 - e
+        e = np.where(np.isfinite(e), e, 0.0)
+        val = np.ldexp(1.0 + f, (e - 7.0).astype(np.int64))
+    return np.where(np.isneginf(z), 0.0, val)
+
+
 def expcast_byte(log2_v) -> np.ndarray:
-    """ExpCast byte of a value given by its base-2 logarithm (no P scale)."""
-    x = 8.0 * np.asarray(log2_v, np.float64) + 56.0 + EXPCAST_BETA
-    return np.clip(np.rint(x), 0, 255).astype(np.uint8)
+    """ExpCast code of a value given by its base-2 logarithm (no P scale).
+
+    The byte position is z = 8 log2(v) + 56 - 0.35 (one multiply-add); the
+    code is the E4M3 rounding (nearest, ties to even, saturating at 448) of
+    byte_map_value(z).  Wherever z >= 7.5 that is round-half-even(z), the
+    article's conversion to an integer.  Below that the position has no E4M3
+    code of its own (codes 1 .. 7 are the subnormals m 2^-9, not on the log
+    map), and the code is the subnormal nearest the byte map's value: one
+    code or less from the exact cast, as in the normal range."""
+    z = 8.0 * np.asarray(log2_v, np.float64) + 56.0 + EXPCAST_BETA
+    return e4m3_encode(byte_map_value(z))
 
 
 def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
                              p_quant: bool = True, p_scale: float = E4M3_MAX,
                              chunk: int = 256, p_cast: str = "exp",
-                             reference: str | None = None, v_block: int = 128,
-                             allowed=None) -> np.ndarray:
+                             v_block: int = 128, allowed=None) -> np.ndarray:
     """Quantisation model of the fp8 attention for one head, in fp64.
 
     Steps: dequantise Q_hat = dec(q8) q_scale, K_hat = dec(k8) k_scale,
@@ -259,16 +286,12 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
     restored per key instead: O_i = sum_j w_ij (V_hat_j + v_bmean_b(j)) / l_i,
     b(j) = j // v_block (the row sum of each block's weights times its mean).
 
-    ``reference`` says which M the weights are taken against: "final" (the
-    row maximum, above) or "running", the online softmax's reference: keys
-    are taken in order in tiles of ``block``; before a tile's weights are
-    written the reference rises to ceil(max t) of the tile if that is larger,
-    and the sums so far are scaled by 2^(M_old - M_new).  For the exp-then-
-    cast path the two agree except for weights in E4M3's subnormal range;
-    the ExpCast byte map is not scale-invariant below byte 8 (the subnormal
-    codes), so for ExpCast the weights depend on the reference they were
-    written against, and the running one (default for ExpCast) is the online
-    method's.
+    The weights are taken against the row maximum M, as the definition
+    of the softmax has it.  An online kernel takes them against a running
+    reference that rises by whole powers of two and rescales its sums; for
+    both casts (exp-then-cast and ExpCast, whose byte map commutes with
+    powers of two) that gives the same weights except where E4M3 rounds to
+    a subnormal, i.e. for weights below 2^-6 / 448 (about 2^-14.8).
     The row sum is that of the weights actually applied to V, so each row's
     weights sum to one and the mean restore of the VC-Attention article
     (section 02, Restore: sum_j P_j v_mean / l = v_mean) holds exactly.
@@ -291,8 +314,6 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.empty((rows.size, D), np.float64)
     log2e = 1.0 / math.log(2.0)
-    if reference is None:
-        reference = "running" if p_cast == "expcast" else "final"
 
     def weights(t, M):
         # masked scores (-inf) weigh 0, also before any allowed key is seen
@@ -309,22 +330,6 @@ def attention_fp8_model_head(qz: dict, scale: float, rows=None, block: int = 64,
             t = (qh[rr] @ keff.T) * (float(np.float64(scale)) * log2e)
             if allowed is not None:
                 t = np.where(allowed(rr), t, -np.inf)
-            if reference == "running":
-                M = np.full((rr.size, 1), -np.inf)
-                acc = np.zeros((rr.size, D))
-                l = np.zeros((rr.size, 1))
-                for j0 in range(0, S, block):
-                    tt = t[:, j0:j0 + block]
-                    Mn = np.maximum(M, np.ceil(tt.max(axis=1, keepdims=True)))
-                    f = np.where(np.isfinite(M), np.exp2(M - Mn), 0.0)
-                    acc *= f
-                    l *= f
-                    M = Mn
-                    w = weights(tt, M)
-                    acc += w @ vh[j0:j0 + block]
-                    l += w.sum(axis=1, keepdims=True)
-                out[r0:r0 + chunk] = acc / l + vm_add
-                continue
             M = np.ceil(t.max(axis=1, keepdims=True))
             w = weights(t, M)
             l = w.sum(axis=1, keepdims=True)

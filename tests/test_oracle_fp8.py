@@ -340,69 +340,44 @@ def test_expcast_total_variation_bound():
         assert tv < bound
 
 
+def expcast_code_bruteforce(x):
+    """ExpCast code of the byte position x, written out on the E4M3 grids:
+    a position at or above 7.5 is its own byte (round half to even); below,
+    the byte map's value 2^(floor(x/8) - 7) (1 + (x/8 - floor(x/8))) is put
+    on the subnormal grid of steps 2^-9 (round half to even), where code c
+    is c 2^-9 (and 8 2^-9 = 2^-6 is the first normal code, byte 8)."""
+    if x == -math.inf:
+        return 0
+    if x >= 7.5:
+        return int(round_half_even(x))
+    e = math.floor(x / 8)
+    val = 2.0 ** (e - 7) * (1 + (x / 8 - e))
+    return int(round_half_even(val * 512))
+
+
 def test_expcast_model_uses_the_direct_bytes():
     """Model with p_cast='expcast' = the textbook weighted mean with the
-    ExpCast weights, written out for a tiny head."""
-    S, D = 12, 128
+    ExpCast weights, written out for a tiny head whose rows reach the
+    subnormal codes."""
+    S, D = 40, 128
     z = _random_qz(S, D, 22, 1)
-    scale = 0.09
+    scale = 2.0
     got = fp8.attention_fp8_model_head(z, scale, p_cast="expcast")
     table = fp8.e4m3_table()
     qh = fp8.e4m3_decode(z["q8"]) * float(z["q_scale"][0])
     kh = fp8.e4m3_decode(z["k8"]) * float(z["k_scale"][0]) + z["k_mean"][0].astype(np.float64)
     vh = fp8.e4m3_decode(z["v8"]) * z["v_scale"].astype(np.float64)
     t = (qh @ kh.T) * scale / math.log(2.0)
+    n_sub = 0
     for i in range(S):
         m = math.ceil(t[i].max())
         x = 8 * (t[i] - m) + 8 * math.log2(448) + 56 - 0.35
-        w = np.array([table[int(min(max(np.rint(xx), 0), 255))] for xx in x])
+        codes = [expcast_code_bruteforce(float(xx)) for xx in x]
+        n_sub += sum(0 < c < 8 for c in codes)
+        w = np.array([table[c] for c in codes])
         o = (w @ vh) / w.sum() + z["v_mean"]
         np.testing.assert_allclose(got[i], o, rtol=1e-12, atol=1e-12)
-
-
-def test_expcast_running_reference_bruteforce():
-    """Online reference (tiles of 64 keys in order): plain loops over tiles
-    and keys; the reference rises only at tiles whose maximum exceeds it, the
-    sums so far are scaled by the power of two, and each tile's bytes are
-    written against the reference then in force."""
-    S, D = 150, 128
-    z = _random_qz(S, D, 23, 1)
-    # keys past the first tile copy their queries, so a row's own key (a
-    # large score q.q) arrives after the first tile
-    z["k8"][64:] = z["q8"][64:]
-    scale = 0.15
-    got = fp8.attention_fp8_model_head(z, scale, p_cast="expcast", rows=np.arange(0, S, 17))
-    table = fp8.e4m3_table()
-    dec = lambda c: float(table[int(c)])
-    log2e = 1.0 / math.log(2.0)
-    kh = [[dec(z["k8"][j, d]) * float(z["k_scale"][j // 64]) + float(z["k_mean"][0, d]) for d in range(D)]
-          for j in range(S)]
-    rose = 0
-    for n, i in enumerate(range(0, S, 17)):
-        qi = [dec(z["q8"][i, d]) * float(z["q_scale"][i // 64]) for d in range(D)]
-        t = [sum(a * b for a, b in zip(qi, kh[j])) * scale * log2e for j in range(S)]
-        m = None
-        acc = [0.0] * D
-        l = 0.0
-        for j0 in range(0, S, 64):
-            mt = math.ceil(max(t[j0:j0 + 64]))
-            if m is None or mt > m:
-                f = 0.0 if m is None else 2.0 ** (m - mt)
-                rose += m is not None
-                acc = [x * f for x in acc]
-                l *= f
-                m = mt
-            for j in range(j0, min(j0 + 64, S)):
-                x = 8 * (t[j] - m) + 8 * math.log2(448) + 56 - 0.35
-                b = int(min(max(round_half_even(x), 0), 255))
-                wj = dec(b) / 448
-                l += wj
-                for d in range(D):
-                    acc[d] += wj * dec(z["v8"][j, d]) * float(z["v_scale"][d])
-        for d in range(0, D, 31):
-            o = acc[d] / l + float(z["v_mean"][d])
-            assert abs(got[n, d] - o) <= 1e-12 * (1 + abs(o))
-    assert rose > 0  # the case exercises a rising reference
+    assert n_sub > 20   # the case exercises the subnormal codes
 
 
 def round_half_even(x):
@@ -412,24 +387,72 @@ def round_half_even(x):
     return r
 
 
-def test_expcast_running_equals_final_when_the_maximum_comes_first():
-    """If every row's maximum lies in the first tile the reference never
-    moves, and the online weights are those against the row maximum."""
-    S, D = 256, 128
-    z = _random_qz(S, D, 24, 1)
-    z["k8"][64:] = (z["k8"][64:] & 0x80) | np.minimum(z["k8"][64:] & 0x7F, 0x20)  # small late keys
-    z["k8"][:64] = (z["k8"][:64] & 0x80) | np.maximum(z["k8"][:64] & 0x7F, 0x50)
-    scale = 0.05
-    run = fp8.attention_fp8_model_head(z, scale, p_cast="expcast", reference="running")
-    fin = fp8.attention_fp8_model_head(z, scale, p_cast="expcast", reference="final")
-    np.testing.assert_allclose(run, fin, rtol=1e-12, atol=1e-12)
+def test_expcast_within_one_code_of_the_exact_cast():
+    """The article's accuracy claim, "otherwise one code off", over the whole
+    range a weight 448 p can take down to where the exact cast reaches zero:
+    log2 v in [-9.5, log2 448], subnormal codes included."""
+    u = np.linspace(-9.5, math.log2(448), 1_000_001)
+    d = fp8.expcast_byte(u).astype(np.int64) - fp8.e4m3_encode(2.0 ** u).astype(np.int64)
+    assert int(np.max(np.abs(d))) == 1
+    sub = u < -6
+    assert np.mean(d[sub] == 0) > 0.5
+
+
+def test_expcast_subnormal_codes_at_known_points():
+    """Closed-form points below the normal range: position x = 8 log2 v +
+    55.65; x = 0 gives 2^-7 (1 + 0) -> code 4 (4 2^-9); x = -8 gives 2^-8 ->
+    code 2; x = -16 gives 2^-9 -> code 1; x = -24 gives 2^-10 = half a step,
+    a tie -> code 0 (even); x = 6 gives 2^-7 (1 + 6/8) = 7 2^-9 -> code 7;
+    x = 7.4 gives 2^-7 (1 + 0.925) = 7.7 2^-9 -> code 8."""
+    for x, code in ((0.0, 4), (-8.0, 2), (-16.0, 1), (-24.0, 0), (6.0, 7), (7.4, 8), (-40.0, 0)):
+        u = (x - 56 + 0.35) / 8
+        assert int(fp8.expcast_byte(np.array([u]))[0]) == code, x
+        assert expcast_code_bruteforce(x) == code, x
+    assert int(fp8.expcast_byte(np.array([-np.inf]))[0]) == 0
+
+
+def test_expcast_weights_commute_with_powers_of_two_in_the_normal_range():
+    """Shifting log2 v by an integer k shifts the byte by 8 k and multiplies
+    the decoded weight by exactly 2^k while both stay normal: an online
+    softmax whose reference rises by whole powers of two writes the same
+    weights as one taken against the final row maximum."""
+    g = np.random.default_rng(31)
+    u = g.uniform(-5.5, 0.0, 200000)
+    table = fp8.e4m3_table()
+    base = fp8.expcast_byte(u).astype(np.int64)
+    for k in (1, 2, 5, 8):
+        shifted = fp8.expcast_byte(u + k).astype(np.int64)
+        np.testing.assert_array_equal(shifted, base + 8 * k)
+        np.testing.assert_array_equal(table[shifted], table[base] * 2.0 ** k)
+
+
+@pytest.mark.parametrize("p_cast", ["exp", "expcast"])
+def test_model_invariant_to_joint_block_permutation(p_cast):
+    """The same permutation of the keys' and values' 64-token blocks (codes,
+    K scales and K means together) leaves every output row unchanged, for
+    both casts (non-causal attention is a sum over keys; VC-Attention
+    article, section 02, Group)."""
+    S, D = 64 * 9, 128
+    nb = S // 64
+    z = _random_qz(S, D, 25, nb)
+    perm = np.random.default_rng(3).permutation(nb)
+    tok = (perm[:, None] * 64 + np.arange(64)[None, :]).ravel()
+    zp = dict(z)
+    zp["k8"], zp["v8"] = z["k8"][tok], z["v8"][tok]
+    zp["k_scale"], zp["k_mean"] = z["k_scale"][perm], z["k_mean"][perm]
+    # the queries keep their own blocks: q_scale is indexed by the query's
+    # block, which does not move
+    for scale in (0.1, 0.6):
+        a = fp8.attention_fp8_model_head(z, scale, p_cast=p_cast)
+        b = fp8.attention_fp8_model_head(zp, scale, p_cast=p_cast)
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
 
 
 @pytest.mark.parametrize("mask", ["causal", "sparse"])
 def test_masked_model_without_p_quantisation_is_masked_attention(mask):
     """With P unquantised, the masked model is the masked definition on the
     dequantised operands; with quantisation every weight of a masked key is 0
-    (exp and ExpCast, final and running references)."""
+    (exp and ExpCast)."""
     g = np.random.default_rng(11)
     S, D = 300, 128
     nb = -(-S // 64)
@@ -457,9 +480,8 @@ def test_masked_model_without_p_quantisation_is_masked_attention(mask):
     v2[hidden] = v2[hidden[::-1]]
     z2["v8"] = v2
     for p_cast in ("exp", "expcast"):
-        for reference in ("final", "running"):
-            kw = dict(p_cast=p_cast, reference=reference, allowed=allowed)
-            a = fp8.attention_fp8_model_head(z, scale, **kw)
-            b = fp8.attention_fp8_model_head(z2, scale, **kw)
-            assert np.all(np.isfinite(a))
-            np.testing.assert_array_equal(a[0], b[0])
+        kw = dict(p_cast=p_cast, allowed=allowed)
+        a = fp8.attention_fp8_model_head(z, scale, **kw)
+        b = fp8.attention_fp8_model_head(z2, scale, **kw)
+        assert np.all(np.isfinite(a))
+        np.testing.assert_array_equal(a[0], b[0])

@@ -137,9 +137,6 @@ def test_model_without_p_quantisation_is_sdpa_on_restored_values():
         *(torch.from_numpy(np.ascontiguousarray(t))[None, None] for t in (qh, kh, vh)), scale=scale)[0, 0].numpy()
     got = fp8.attention_fp8_model_head(z, scale, p_quant=False)
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
-    # the running-reference form of the model agrees (same weights here)
-    got_r = fp8.attention_fp8_model_head(z, scale, p_quant=False, reference="running")
-    np.testing.assert_allclose(got_r, ref, rtol=1e-10, atol=1e-11)
 
 
 def test_quantised_weights_bruteforce_tiny():
