@@ -101,14 +101,42 @@ def read_sclk(path):
     return None
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "video_diffusion_transformer_vdit_amd", "csrc", "attn_bf16.hip")
+CSRC = os.path.join(ROOT, "video_diffusion_transformer_vdit_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "attn_bf16.hip")
+FP8_SOURCE = os.path.join(CSRC, "attn_fp8.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_kernel__wan2.1-14b-720p__hbm_traffic.txt")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_kernels__wan2.1-14b-720p__valu_mfma_counters.txt")
 
 
 def source_sha256(path=KERNEL_SOURCE):
     import hashlib
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_counters():
+    """Per-kernel counter figures (clock, MFMA busy, VALU active, LDS active)
+    from the committed counter summary, keyed by kernel name; only kernels
+    whose source file still has the recorded sha256 are returned."""
+    if not os.path.exists(COUNTER_FILE):
+        return {}
+    shas, rows = {}, {}
+    cols = None
+    with open(COUNTER_FILE) as f:
+        for line in f:
+            if line.startswith("# ") and "sha256:" in line:
+                name, _, sha = line[2:].partition("sha256:")
+                shas[name.strip()] = sha.strip()
+            elif line.startswith("# kernel |"):
+                cols = [c.strip() for c in line[2:].split("|")]
+            elif cols and not line.startswith("#") and line.strip():
+                parts = line.split()
+                name = parts[0]
+                if len(parts) == len(cols):
+                    rows[name] = dict(zip(cols[1:], (float(x) for x in parts[1:])))
+    ok = {"attn_fwd_bf16": shas.get("attn_bf16.hip") == source_sha256(KERNEL_SOURCE),
+          "attn_fwd_fp8": shas.get("attn_fp8.hip") == source_sha256(FP8_SOURCE)}
+    return {k: v for k, v in rows.items() if any(k.startswith(p) and good for p, good in ok.items())}
 
 
 def measured_traffic():
@@ -146,13 +174,17 @@ def calibration_copy(n_bytes=1 << 31, reps=3):
 
 def cpu_baseline(w, q, k, v, scale, seconds):
     """fp64 oracle (as it stands) on head 0, 256-row chunks until `seconds`
-    have elapsed; rate scaled to TFLOP/s of the same attention arithmetic."""
+    have elapsed; rate scaled to TFLOP/s of the same attention arithmetic.
+    The oracle's matrix products run on numpy's BLAS threads, so `cores` is
+    that thread count; the host's logical CPUs and the process's affinity
+    set are reported beside it."""
     from oracle import attention as oa
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads = affinity
     rows_done = 0
     t0 = time.perf_counter()
     chunk = 256
@@ -170,10 +202,54 @@ def cpu_baseline(w, q, k, v, scale, seconds):
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "blas_threads": int(threads),
+        "cpu_count": os.cpu_count(),
+        "affinity_cpus": affinity,
         "kind": "oracle",
         "sample": (f"{rows_done} query rows of head 0 of {w.name} (S={w.S}), fp64 numpy, "
                    f"{dt:.1f} s; full call extrapolates to {w.flop / (flop / dt):.0f} s"),
     }
+
+
+CONFIGS = ("tiny-3x16x16", "wan2.1-1.3b-480p", "wan2.2-720p-16x")
+
+
+def other_configs(steps, warmup, fp8=True):
+    """bf16 attention (and the fp8 pre-pass + attention) on the workloads
+    other than the headline, timed the same way: TFLOP/s and the fraction of
+    the dense peak of the arithmetic's type."""
+    import torch
+    out = {}
+    for name in CONFIGS:
+        w = inputs.get_workload(name)
+        scale = float(np.float32(1.0 / math.sqrt(w.D)))
+        log(f"[bench] {name} {w.shape}")
+        qb, kb, vb = inputs.make_inputs(w)
+        q, k, v = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda() for b in (qb, kb, vb))
+        del qb, kb, vb
+        o = torch.empty_like(q)
+        # the tiny workload runs for microseconds: more launches to time
+        n = steps * (50 if w.S < 4096 else 1)
+        ms = time_launches(lambda: binding.vdit_attn_fwd(q, k, v, o=o, scale=scale), n, warmup)
+        tf = w.flop / (ms * 1e-3) / 1e12
+        r = {"shape": list(w.shape), "bf16_ms": round(ms, 4), "bf16_tflops": round(tf, 2),
+             "bf16_peak_fraction": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if fp8:
+            z = binding.vdit_attn_quant_fp8(q, k, v)
+            ms_a = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o), n, warmup)
+            ms_x = time_launches(lambda: binding.vdit_attn_fwd_fp8(z, scale=scale, o=o, expcast=True),
+                                 n, warmup)
+            for key, t in (("fp8", ms_a), ("fp8_expcast", ms_x)):
+                tf8 = w.flop / (t * 1e-3) / 1e12
+                r[key + "_ms"] = round(t, 4)
+                r[key + "_tflops"] = round(tf8, 2)
+                r[key + "_peak_fraction"] = round(tf8 / PEAK_FP8_TFLOPS, 4)
+            del z
+        out[name] = r
+        del q, k, v, o
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -184,6 +260,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the bf16/fp8 timings of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a 2 GiB device copy (counter calibration) and exit")
@@ -218,6 +296,10 @@ def main():
                                            args.steps, args.warmup, detail=True)
     tflops = w.flop / (ms * 1e-3) / 1e12
     sclk = float(np.median(clocks)) if clocks else None
+    headline = w.name == HEADLINE
+    counters = measured_counters() if headline else {}
+    cnt_bf16 = counters.get("attn_fwd_bf16_kernel<0>", {})
+    traffic = measured_traffic() if headline else None
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -241,9 +323,15 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic() if w.name == HEADLINE else None,
+            "traffic": traffic,
+            "hbm_gbs": round(traffic / (ms * 1e-3) / 1e9, 1) if traffic else None,
             "algorithmic_flop_per_launch": w.flop,
             "algorithmic_bytes_per_launch": 4 * w.B * w.H * w.S * w.D * 2,
+            # from the committed counter pass on the same kernel source
+            # (rocprofv3 --pmc; null once the source has changed)
+            "mfma_busy": cnt_bf16.get("mfma_busy"),
+            "valu_active": cnt_bf16.get("valu_active"),
+            "counter_clock_ghz": cnt_bf16.get("clock_GHz"),
         },
         "launch_ms": {"median": round(float(np.median(per_launch)), 4),
                       "min": round(min(per_launch), 4), "max": round(max(per_launch), 4)},
@@ -313,6 +401,12 @@ def main():
             "expcast_attention_tflops": round(w.flop / (ms_x * 1e-3) / 1e12, 2),
             "expcast_attention_peak_fraction": round(w.flop / (ms_x * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
         }
+        for key, kname in (("attention", "attn_fwd_fp8_kernel<true,false,false,0>"),
+                           ("expcast_attention", "attn_fwd_fp8_kernel<true,true,false,0>")):
+            c = counters.get(kname, {})
+            result["fp8"][key + "_counters"] = {"mfma_busy": c.get("mfma_busy"),
+                                                "valu_active": c.get("valu_active"),
+                                                "clock_ghz": c.get("clock_GHz")} if c else None
         log("[bench] fp8 block-causal and block-sparse attention (same chunk and map as bf16)")
         for name, kw, flop in (("block_causal", {"chunk": chunk}, causal_flop),
                                ("block_sparse", {"block_mask": mask_dev}, sparse_flop)):
@@ -349,8 +443,11 @@ def main():
             "permute_tokens_ms": round(ms_p, 4),
         })
         del z, zv, o8, kp, perm
-    del o, mask_dev
+    del o, mask_dev, q, k, v
     torch.cuda.synchronize()
+
+    if not args.no_configs and headline:
+        result["configs"] = other_configs(args.steps, args.warmup, not args.no_fp8)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

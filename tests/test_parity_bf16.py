@@ -76,6 +76,33 @@ def test_scales():
         check_close(got, oa.attention(*x, scale), f"scale={scale}", ulp_slack=True)
 
 
+def test_large_scale_returns_the_argmax_row():
+    """Large scale with a unique maximum gives the value row of the best key
+    (the softmax's limit).  At scale 50 a row whose best score leads the
+    second by margin m gives every other key a weight under 2^(-50 m log2 e);
+    rows with that exponent past 24 (far below bf16's 2^-9) must return the
+    best key's value row bit for bit, and every row meets the oracle
+    (one-bf16-step slack)."""
+    g = np.random.default_rng(9)
+    B, H, S, scale = 1, 2, 300, 50.0
+    q, k, v = (inputs.f32_to_bf16_bits(g.standard_normal((B, H, S, 128)).astype(np.float32))
+               for _ in range(3))
+    got_bits = bits_of(run(q, k, v, scale=scale))
+    checked = 0
+    for h in range(H):
+        s = oa.widen_bf16(q[0, h]) @ oa.widen_bf16(k[0, h]).T
+        order = np.argsort(s, axis=1)
+        best, second = order[:, -1], order[:, -2]
+        margin = (s[np.arange(S), best] - s[np.arange(S), second]) * scale / math.log(2.0)
+        sure = margin > 24
+        assert sure.mean() > 0.8
+        np.testing.assert_array_equal(got_bits[0, h][sure], v[0, h][best[sure]])
+        checked += int(sure.sum())
+    log(f"large scale: {checked} rows equal their arg-max value row")
+    check_close(inputs.bf16_bits_to_f32(got_bits).astype(np.float64), oa.attention(q, k, v, scale),
+                "scale=50", ulp_slack=True)
+
+
 def test_single_key_returns_value_exactly():
     g = np.random.default_rng(1)
     x = [inputs.f32_to_bf16_bits(g.standard_normal((1, 3, 1, 128)).astype(np.float32)) for _ in range(3)]

@@ -3,8 +3,13 @@
 * The pre-pass is integer work decided in a stated precision: codes, scales
   and means must equal the oracle's bit for bit.
 * The fp8 attention kernel, fed the oracle's quantised tensors, is compared
-  with the fp64 quantisation model: cosine >= 0.999, max-abs <= 5e-2 and L1
-  mean-rel <= 1e-2 against the model rounded to bf16.
+  with the fp64 quantisation model rounded to bf16: the method's bars
+  (cosine >= 0.999, max-abs <= 5e-2) and the kernel-vs-model bars (cosine >=
+  0.99999, L1 mean-rel <= 2.5e-3, every row's relative L2 error bounded).
+* Reordering the 64-token key blocks of the pre-pass outputs (K and V codes,
+  K scales and K means together) leaves the output within rounding, for
+  exp-then-cast and ExpCast weights alike (VC-Attention article, section 02,
+  Group: non-causal attention is a sum over keys).
 * End to end (GPU pre-pass + GPU attention) against the unquantised truth the
   error must stay within the floor that ideal quantisation itself reaches
   (the model's own error against the truth on the same rows), plus a margin.
@@ -19,7 +24,8 @@ from oracle import attention as oa
 from oracle import fp8 as ofp8
 from video_diffusion_transformer_vdit_amd import binding, inputs
 
-from gpu_util import (FP8_COS, FP8_MAX_ABS, FP8_MODEL_MEAN_REL, f32_of, log, round_bf16,
+from gpu_util import (FP8_REORDER_MEAN_REL, check_fp8_model, f32_of, log, permute_key_blocks,
+                      round_bf16,
                       sample_rows, tile_v8, to_dev, to_dev_any, untile_v8, workload_heads)
 
 pytestmark = pytest.mark.gpu
@@ -147,12 +153,7 @@ def test_prepass_bit_exact_workload(name):
 
 
 def check_model(got, ref, what):
-    ref_b = round_bf16(ref)
-    cos = ofp8.cosine(got, ref_b)
-    ma = ofp8.max_abs(got, ref_b)
-    mr = ofp8.mean_rel_l1(got, ref_b)
-    log(f"{what} vs quant model: cos={cos:.7f} max_abs={ma:.3e} mean_rel={mr:.3e}")
-    assert cos >= FP8_COS and ma <= FP8_MAX_ABS and mr <= FP8_MODEL_MEAN_REL, what
+    check_fp8_model(got, ref, what)
 
 
 def quantize_threaded(q, k, v, threads=8):
@@ -274,6 +275,55 @@ def test_expcast_workload_vs_model_and_truth():
             f"ExpCast-model floor cos={fl_cos:.6f} max_abs={fl_ma:.3e}")
         assert 1 - cos <= 1.5 * (1 - fl_cos) + 1e-5
         assert ma <= 1.5 * fl_ma + 1e-3
+
+
+def test_fp8_joint_key_block_permutation_720p():
+    """The 720p workload through the GPU pre-pass; the 1,181 full 64-token key
+    blocks of its outputs reversed (K and V codes, K scales, K means; the
+    ragged last block stays last).  Full attention with exp-then-cast and
+    with ExpCast weights, and block-sparse attention under the benchmark's map
+    with its columns permuted alike, must move by rounding only: the fp8
+    MFMA regroups the products it sums (sampled rows of three heads, L1
+    mean-rel <= 5e-4 between the two orders), and ExpCast moves no more than
+    exp-then-cast (within 1.5x).  The reordered run also meets the model of
+    the original order."""
+    import torch
+    w = inputs.get_workload("wan2.1-14b-720p-fp8")
+    q, k, v = inputs.make_inputs(w)
+    z = gpu_quant(q, k, v)
+    nfull = w.S // 64
+    zp, idx64 = permute_key_blocks(z, np.arange(nfull)[::-1], 64)
+    mask = inputs.make_block_mask(w.B, w.H, w.S, 0.25, seed=w.seed)
+    mask_d = torch.from_numpy(mask).cuda()
+    mask_p = torch.from_numpy(np.ascontiguousarray(mask[..., idx64])).cuda()
+    rows = sample_rows(w.S, n_random=48)
+    heads = workload_heads(w.H)
+    got, moved = {}, {}
+    for ec in (False, True):
+        for kind in ("dense", "sparse"):
+            kw = {} if kind == "dense" else {"block_mask": mask_d}
+            kwp = {} if kind == "dense" else {"block_mask": mask_p}
+            log(f"fp8 720p block order, {kind}, expcast={ec}")
+            a = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec, **kw)
+            b = binding.vdit_attn_fwd_fp8(zp, scale=SCALE, expcast=ec, **kwp)
+            torch.cuda.synchronize()
+            ga = a[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+            gb = b[0][heads][:, rows].float().cpu().numpy().astype(np.float64)
+            del a, b
+            mr, ma = ofp8.mean_rel_l1(gb, ga), ofp8.max_abs(gb, ga)
+            log(f"  reversed key blocks vs in order: mean_rel={mr:.3e} max_abs={ma:.3e}")
+            assert mr <= FP8_REORDER_MEAN_REL, (kind, ec)
+            moved[(kind, ec)] = mr
+            got[(kind, ec)] = gb
+    for kind in ("dense", "sparse"):
+        assert moved[(kind, True)] <= 1.5 * moved[(kind, False)] + 2e-5, kind
+    del z, zp
+    torch.cuda.empty_cache()
+    h = heads[0]
+    zh = ofp8.quantize_head(q[0, h], k[0, h], v[0, h])
+    for ec in (False, True):
+        model = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows, p_cast="expcast" if ec else "exp")
+        check_model(got[("dense", ec)][0], model, f"reversed key blocks, head {h}, expcast={ec}")
 
 
 def test_fp8_max_sequence_length_sampled():

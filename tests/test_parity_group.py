@@ -156,7 +156,10 @@ def test_grouping_raises_the_energy_vsmooth_removes():
 
 def test_workload_grouping():
     """720p values (40 heads x 75,600 tokens, 591 clusters, 4 rounds): valid
-    stable permutations; grouping does not lower the block energy removed."""
+    stable permutations, and grouping raises the share of the energy the
+    128-token block means remove by a wide margin (the article's effect: 8%
+    to 36% on real activations; here the four outlier channels per head,
+    scaled by 8, give the clusters their structure)."""
     import torch
     w = inputs.get_workload("wan2.1-14b-720p")
     _, _, v = inputs.make_inputs(w)
@@ -170,4 +173,4 @@ def test_workload_grouping():
         vf = oa.widen_bf16(v[0, h])
         before, after = og.block_energy_removed(vf), og.block_energy_removed(vf, p[0, h])
         log(f"720p head {h}: block energy removed {before:.4f} -> {after:.4f}")
-        assert after >= before
+        assert after >= before + 0.25 and after >= 0.3

@@ -85,6 +85,20 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Context for the tensors a call allocates (outputs, workspaces): on the
+    stream the call launches on, so that torch's caching allocator, which
+    tracks blocks per stream, does not hand them to other streams' work while
+    the call's kernels are still queued.  Inert for the current stream."""
+    import contextlib
+    import torch
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream)
+    return torch.cuda.stream(stream)
+
+
 def _dev(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor):
@@ -111,7 +125,8 @@ def vdit_attn_fwd(q, k, v, o=None, scale=None, stream=None):
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
     if o is None:
-        o = torch.empty_like(q)
+        with _alloc_on(stream):
+            o = torch.empty_like(q)
     scale = D ** -0.5 if scale is None else float(scale)
     lib = load()
     check(lib.vdit_attn_fwd(_dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
@@ -128,7 +143,8 @@ def vdit_attn_fwd_block_causal(q, k, v, chunk, o=None, scale=None, stream=None):
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
     if o is None:
-        o = torch.empty_like(q)
+        with _alloc_on(stream):
+            o = torch.empty_like(q)
     scale = D ** -0.5 if scale is None else float(scale)
     lib = load()
     check(lib.vdit_attn_fwd_block_causal(
@@ -155,7 +171,8 @@ def vdit_attn_fwd_block_sparse(q, k, v, block_mask, o=None, scale=None, stream=N
     if block_mask.dtype == torch.bool:
         block_mask = block_mask.view(torch.uint8)
     if o is None:
-        o = torch.empty_like(q)
+        with _alloc_on(stream):
+            o = torch.empty_like(q)
     scale = D ** -0.5 if scale is None else float(scale)
     lib = load()
     check(lib.vdit_attn_fwd_block_sparse(
@@ -209,7 +226,11 @@ def vdit_attn_quant_fp8(q, k, v, k_mean_blocks=None, out=None, stream=None, v_me
     B, H, S, D = _shape4(q)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
-    z = quant_buffers(B, H, S, k_mean_blocks, q.device, v_mean) if out is None else out
+    if out is None:
+        with _alloc_on(stream):
+            z = quant_buffers(B, H, S, k_mean_blocks, q.device, v_mean)
+    else:
+        z = out
     kmb = int(z["k_mean"].shape[2])
     lib = load()
     if "v_bmean" in z:
@@ -244,7 +265,8 @@ def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False, chunk=0
     import torch
     B, H, S, D = _shape4(z["q8"])
     if o is None:
-        o = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=z["q8"].device)
+        with _alloc_on(stream):
+            o = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=z["q8"].device)
     scale = D ** -0.5 if scale is None else float(scale)
     kmb = int(z["k_mean"].shape[2])
     lib = load()
@@ -296,10 +318,11 @@ def vdit_vsmooth_group(v, n_clusters=None, rounds=4, stream=None):
     ws_bytes = int(lib.vdit_vsmooth_group_workspace_size(B, H, S, D, k))
     if ws_bytes == 0:
         raise ValueError("invalid shape or n_clusters for V-Smooth Group")
-    perm = torch.empty((B, H, S), dtype=torch.int32, device=v.device)
-    labels = torch.empty((B, H, S), dtype=torch.int32, device=v.device)
-    cent = torch.empty((B, H, k, D), dtype=torch.float32, device=v.device)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=v.device)
+    with _alloc_on(stream):
+        perm = torch.empty((B, H, S), dtype=torch.int32, device=v.device)
+        labels = torch.empty((B, H, S), dtype=torch.int32, device=v.device)
+        cent = torch.empty((B, H, k, D), dtype=torch.float32, device=v.device)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=v.device)
     check(lib.vdit_vsmooth_group(
         _dev(v, torch.bfloat16, "v"), _dev(perm, torch.int32, "perm"),
         _dev(labels, torch.int32, "labels"), _dev(cent, torch.float32, "centroids"),
@@ -314,7 +337,8 @@ def vdit_permute_tokens(x, perm, out=None, stream=None):
     if tuple(perm.shape) != (B, H, S):
         raise ValueError("perm must have shape [B, H, S]")
     if out is None:
-        out = torch.empty_like(x)
+        with _alloc_on(stream):
+            out = torch.empty_like(x)
     lib = load()
     check(lib.vdit_permute_tokens(_dev(x, torch.bfloat16, "x"), _dev(perm, torch.int32, "perm"),
                                   _dev(out, torch.bfloat16, "out"), B, H, S, D, _stream(stream)))

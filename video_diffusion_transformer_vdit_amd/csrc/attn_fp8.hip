@@ -41,7 +41,7 @@
 // workgroup per CU; scores transposed (S^T = K Q^T) so each lane owns one
 // query; K tiles (row-major, 16-byte chunks XOR-swizzled by key & 7) and V
 // tiles (already transposed and permuted by the pre-pass) go global -> LDS by
-// DMA into four-deep rings (three-deep with V block means); waves 0-3 and
+// DMA into four-deep rings; waves 0-3 and
 // 4-7 run the exponential phase and the MFMA phase of each tile one phase
 // apart (ping-pong).  The block-causal and block-sparse key masks follow the
 // bf16 kernel's schedules.
@@ -60,9 +60,28 @@ constexpr int kCompBlocks = 32;             // K-mean blocks per compensation ba
 constexpr float kLog2P8 = 8.807354922057604f;  // log2(448)
 // ExpCast-FP8: the E4M3 byte of a value v, read as an integer, is about
 // 8 log2(v) + 56 (VC-Attention article, section 03); with the article's
-// centring constant -0.35 and P scaled by 448, the byte of 448 p with
-// log2 p = t - m is rne(8 (t - m) + 8 log2(448) + 55.65).
+// centring constant -0.35 and P scaled by 448, the byte position of 448 p
+// with log2 p = t - m is z = 8 (t - m) + 8 log2(448) + 55.65.  A normal byte
+// 8 e + m stands for 2^(e - 7) (1 + m / 8); the same rule at a real position
+// z is the fp32 value whose bit pattern is z 2^20 + 120 2^23 (exponent field
+// floor(z / 8) + 120, mantissa (z mod 8) 2^20).  The kernel forms that
+// pattern with one FMA per weight and lets the hardware E4M3 convert round
+// it: in the normal range (z >= 7.5) the code is rne(z), the article's byte;
+// below it, where bytes 1-7 are subnormals (m 2^-9) rather than points of
+// the log map, it is the subnormal nearest the map's value, within one code
+// of the exact cast, so the weights scale by exact powers of two with the
+// online reference just as exp-then-cast weights do.
 constexpr float kExpCastOffset = 8.0f * 8.807354922057604f + 56.0f - 0.35f;
+constexpr float kTwo20 = 1048576.0f;       // 2^20: one byte position in fp32 bits
+constexpr float kBias120 = 1006632960.0f;  // 120 2^23: exponent field of byte 0's octave
+
+// fp32 -> u32, saturating: negative values and -inf give 0 (v_cvt_u32_f32).
+// Written as asm: the C++ conversion of a negative value is undefined.
+__device__ __forceinline__ uint32_t cvt_u32_sat(float x) {
+  uint32_t r;
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
 
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // operand formats 0/0 = E4M3 x E4M3; no block scales
@@ -110,11 +129,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k2[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_k3[kRing == 4 ? kTileBytes : 1];
+  __shared__ __attribute__((aligned(1024))) char lds_k3[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v2[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v3[kRing == 4 ? kTileBytes : 1];
+  __shared__ __attribute__((aligned(1024))) char lds_v3[kTileBytes];
   __shared__ float lds_comp[kWaves][kCompBlocks][32];
   constexpr bool kStageKm = kBlockMean;
   __shared__ __attribute__((aligned(1024))) char lds_km[kStageKm ? kCompBlocks * 512 : 1];
@@ -480,20 +499,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       m_ref = mnext;
     }
     if (kExpCast) {
-      // byte = rne(8 (t - m) + offset), one FMA and one saturating convert
-      // (v_cvt_pk_u8_f32: round to nearest even, clamp to [0, 255]); t <= m
-      // keeps it <= 126, the code of 448
-      const float a8 = 8.0f * a, b8 = 8.0f * (cb - m_ref) + kExpCastOffset;
+      // bits of the byte map's value at z = 8 (t - m) + offset: one FMA to
+      // z 2^20 + 120 2^23 (an integer-valued float, exact to 2^-14 in z), a
+      // saturating convert to u32 (masked keys, -inf, give 0), the E4M3
+      // rounding by the hardware convert.  t <= m keeps z <= 126.1, so the
+      // code is at most 126, the code of 448.
+      const float a20 = (8.0f * kTwo20) * a;
+      const float b20 = fmaf(8.0f * (cb - m_ref) + kExpCastOffset, kTwo20, kBias120);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          // all four bytes are written: start from the first input's bits
-          const float x0 = fmaf(s[kb][4 * p], a8, b8);
-          uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(x0, 0, __float_as_uint(x0));
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 1], a8, b8), 1, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 2], a8, b8), 2, w);
-          pk[4 * kb + p] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[kb][4 * p + 3], a8, b8), 3, w);
+          const float v0 = __uint_as_float(cvt_u32_sat(fmaf(s[kb][4 * p], a20, b20)));
+          const float v1 = __uint_as_float(cvt_u32_sat(fmaf(s[kb][4 * p + 1], a20, b20)));
+          const float v2 = __uint_as_float(cvt_u32_sat(fmaf(s[kb][4 * p + 2], a20, b20)));
+          const float v3 = __uint_as_float(cvt_u32_sat(fmaf(s[kb][4 * p + 3], a20, b20)));
+          // the second convert fills the high half: start from v0's bits
+          uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, (int)__float_as_uint(v0), false);
+          pk[4 * kb + p] = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
         }
     } else {
       const float bias = cb + kLog2P8 - m_ref;
@@ -556,10 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // all but the newest kRing - 2 batches (two loads each): a batch issued in
   // phase 2 of step t is first read in phase 2 of step t + kRing - 1
   auto wait_loads = [&]() __attribute__((always_inline)) {
-    if (kRing == 4)
-      __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
+    __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
   };
   auto phase1 = [&](int t) __attribute__((always_inline)) {
     if (kVBlock && (t % 32) == 0 && t > 0) vload((t >> 5) - 1);
@@ -615,10 +635,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   issue_k(tile_of(1), lds_k1);
   issue_v(tile_of(1), lds_v1);
   issue_k(tile_of(2), lds_k2);
-  if (kRing == 4) {
-    issue_v(tile_of(2), lds_v2);
-    issue_k(tile_of(3), lds_k3);
-  }
+  issue_v(tile_of(2), lds_v2);
+  issue_k(tile_of(3), lds_k3);
   if (kStageKm) km_issue(0);
   if (kBlockMean && !kStageKm) kmean_batch(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -637,46 +655,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   // Step t reads K(t+1) and V(t) and refills the buffers of K(t) and V(t-1)
   // with K(t+kRing) and V(t+kRing-1).
   int t = 0;
-  if (kRing == 4) {
-    for (; t + 4 <= nkt; t += 4) {
-      phase1(t);
-      phase2(t, lds_k1, lds_v0, lds_k0, lds_v3);
-      phase1(t + 1);
-      phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
-      phase1(t + 2);
-      phase2(t + 2, lds_k3, lds_v2, lds_k2, lds_v1);
-      phase1(t + 3);
-      phase2(t + 3, lds_k0, lds_v3, lds_k3, lds_v2);
-    }
-    if (t < nkt) {
-      phase1(t);
-      phase2(t, lds_k1, lds_v0, lds_k0, lds_v3);
-    }
-    if (t + 1 < nkt) {
-      phase1(t + 1);
-      phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
-    }
-    if (t + 2 < nkt) {
-      phase1(t + 2);
-      phase2(t + 2, lds_k3, lds_v2, lds_k2, lds_v1);
-    }
-  } else {
-    for (; t + 3 <= nkt; t += 3) {
-      phase1(t);
-      phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
-      phase1(t + 1);
-      phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
-      phase1(t + 2);
-      phase2(t + 2, lds_k0, lds_v2, lds_k2, lds_v1);
-    }
-    if (t < nkt) {
-      phase1(t);
-      phase2(t, lds_k1, lds_v0, lds_k0, lds_v2);
-    }
-    if (t + 1 < nkt) {
-      phase1(t + 1);
-      phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
-    }
+  for (; t + 4 <= nkt; t += 4) {
+    phase1(t);
+    phase2(t, lds_k1, lds_v0, lds_k0, lds_v3);
+    phase1(t + 1);
+    phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+    phase1(t + 2);
+    phase2(t + 2, lds_k3, lds_v2, lds_k2, lds_v1);
+    phase1(t + 3);
+    phase2(t + 3, lds_k0, lds_v3, lds_k3, lds_v2);
+  }
+  if (t < nkt) {
+    phase1(t);
+    phase2(t, lds_k1, lds_v0, lds_k0, lds_v3);
+  }
+  if (t + 1 < nkt) {
+    phase1(t + 1);
+    phase2(t + 1, lds_k2, lds_v1, lds_k1, lds_v0);
+  }
+  if (t + 2 < nkt) {
+    phase1(t + 2);
+    phase2(t + 2, lds_k3, lds_v2, lds_k2, lds_v1);
   }
   if (group_a) barrier();  // matches group B's extra one
   // no DMA may still be writing this workgroup's LDS when it exits
