@@ -133,6 +133,33 @@ vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v,
 size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean_blocks);
 
 /*
+ * Allocation-free vdit_attn_quant_fp8, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, outputs and errors as
+ * vdit_attn_quant_fp8 without the workspace: the per-block statistics live in
+ * the library's own device scratch, a static array of
+ * vdit_attn_quant_fp8_noalloc_max_workspace() bytes (128 MiB; the 720p
+ * workload, 40 heads x 75,600 tokens with one K mean per 64-token block,
+ * needs 96.9 MB) that every GPU the library runs on holds until the process
+ * ends.  A shape whose vdit_attn_quant_fp8_workspace_size exceeds it gives
+ * VDIT_ERR_UNSUPPORTED before any HIP call.  The call allocates nothing and
+ * the scratch needs no clearing (every statistic it reads is written by the
+ * same call).  The stream must belong to the current device (else
+ * VDIT_ERR_HIP).  All calls on one GPU share its scratch: calls that overlap
+ * in time on one GPU (different streams, or host threads) race and must be
+ * ordered by the caller.
+ */
+vdit_status vdit_attn_quant_fp8_noalloc(const void* q, const void* k, const void* v,
+                                        void* q8, void* k8, void* v8,
+                                        float* q_scale, float* k_scale,
+                                        float* k_mean, int k_mean_blocks,
+                                        float* v_mean, float* v_scale,
+                                        int B, int H, int S, int D, void* stream);
+
+/* Size in bytes of the scratch behind vdit_attn_quant_fp8_noalloc. */
+size_t vdit_attn_quant_fp8_noalloc_max_workspace(void);
+
+/*
  * fp8 attention forward on the pre-pass outputs (same shapes and layouts as
  * above, v8 tiled).
  * Scores: s_ij = q_scale_b(i) k_scale_b(j) (q8_i . k8_j) + q_hat_i . k_mean_b(j)

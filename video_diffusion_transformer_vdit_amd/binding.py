@@ -31,6 +31,9 @@ SIGNATURES = {
     "vdit_attn_quant_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _Z,
                                  _I, _I, _I, _I, _P]),
     "vdit_attn_quant_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "vdit_attn_quant_fp8_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                         _I, _I, _I, _I, _P]),
+    "vdit_attn_quant_fp8_noalloc_max_workspace": (_Z, []),
     "vdit_attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
     "vdit_attn_fwd_fp8_expcast": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
     "vdit_attn_quant_fp8_vsmooth": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _Z,
@@ -252,6 +255,27 @@ def vdit_attn_quant_fp8(q, k, v, k_mean_blocks=None, out=None, stream=None, v_me
         kmb, _dev(z["v_mean"], torch.float32, "v_mean"), _dev(z["v_scale"], torch.float32, "v_scale"),
         _dev(z["workspace"], torch.uint8, "workspace"), z["workspace"].numel(),
         B, H, S, D, _stream(stream)))
+    return z
+
+
+def vdit_attn_quant_fp8_noalloc(q, k, v, out, stream=None):
+    """The fp8 pre-pass through the allocation-free entry point: the caller
+    passes the outputs (``out``, a dict as from quant_buffers with v_mean;
+    its workspace is not used) and the library's own device scratch holds
+    the intermediate statistics.  Returns ``out``."""
+    import torch
+    B, H, S, D = _shape4(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    z = out
+    lib = load()
+    check(lib.vdit_attn_quant_fp8_noalloc(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(z["q8"], torch.uint8, "q8"), _dev(z["k8"], torch.uint8, "k8"),
+        _dev(z["v8"], torch.uint8, "v8"), _dev(z["q_scale"], torch.float32, "q_scale"),
+        _dev(z["k_scale"], torch.float32, "k_scale"), _dev(z["k_mean"], torch.float32, "k_mean"),
+        int(z["k_mean"].shape[2]), _dev(z["v_mean"], torch.float32, "v_mean"),
+        _dev(z["v_scale"], torch.float32, "v_scale"), B, H, S, D, _stream(stream)))
     return z
 
 

@@ -117,11 +117,13 @@ vdit_status vdit_attn_fwd_block_sparse(const void* q, const void* k, const void*
   return fwd_bf16(q, k, v, o, B, H, S, D, scale, 0, block_mask, dtype, stream);
 }
 
+// use_scratch: the allocation-free entry point, whose workspace is the
+// library's own device scratch instead of a caller argument.
 static vdit_status quant_fp8(const void* q, const void* k, const void* v, void* q8, void* k8,
                              void* v8, float* q_scale, float* k_scale, float* k_mean,
                              int k_mean_blocks, float* v_mean, void* v_bmean, float* v_scale,
                              void* workspace, size_t workspace_bytes, int B, int H, int S, int D,
-                             void* stream) {
+                             void* stream, bool use_scratch = false) {
   VDIT_TRY(check_ptr(q, "q"));
   VDIT_TRY(check_ptr(k, "k"));
   VDIT_TRY(check_ptr(v, "v"));
@@ -136,13 +138,25 @@ static vdit_status quant_fp8(const void* q, const void* k, const void* v, void* 
   else
     VDIT_TRY(check_fptr(v_mean, "v_mean"));
   VDIT_TRY(check_fptr(v_scale, "v_scale"));
-  VDIT_TRY(check_ptr(workspace, "workspace"));
+  if (!use_scratch) VDIT_TRY(check_ptr(workspace, "workspace"));
   VDIT_TRY(check_shape(B, H, S, D));
   const int nb = (S + VDIT_FP8_BLOCK - 1) / VDIT_FP8_BLOCK;
   if (k_mean_blocks != 1 && k_mean_blocks != nb)
     return fail(VDIT_ERR_UNSUPPORTED, "%s", "k_mean_blocks must be 1 or ceil(S/64)");
-  if (workspace_bytes < vdit::quant_fp8_workspace_bytes(B, H, S, k_mean_blocks))
+  const size_t need = vdit::quant_fp8_workspace_bytes(B, H, S, k_mean_blocks);
+  if (use_scratch) {
+    if (need > vdit::noalloc_scratch_bytes()) {
+      char msg[160];
+      std::snprintf(msg, sizeof(msg), "the pre-pass needs %zu bytes of scratch; the allocation-free "
+                    "entry point holds %zu (use vdit_attn_quant_fp8 with a workspace)",
+                    need, vdit::noalloc_scratch_bytes());
+      return fail(VDIT_ERR_UNSUPPORTED, "%s", msg);
+    }
+    const hipError_t e = vdit::noalloc_scratch(static_cast<hipStream_t>(stream), &workspace);
+    if (e != hipSuccess) return hip_result(e);
+  } else if (workspace_bytes < need) {
     return fail(VDIT_ERR_INVALID_ARG, "%s", "workspace too small");
+  }
   return hip_result(vdit::launch_quant_fp8(q, k, v, q8, k8, v8, q_scale, k_scale, k_mean,
                                            k_mean_blocks, v_mean, v_bmean, v_scale, workspace, B,
                                            H, S, static_cast<hipStream_t>(stream)));
@@ -157,6 +171,17 @@ vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v, voi
   return quant_fp8(q, k, v, q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, nullptr,
                    v_scale, workspace, workspace_bytes, B, H, S, D, stream);
 }
+
+vdit_status vdit_attn_quant_fp8_noalloc(const void* q, const void* k, const void* v, void* q8,
+                                        void* k8, void* v8, float* q_scale, float* k_scale,
+                                        float* k_mean, int k_mean_blocks, float* v_mean,
+                                        float* v_scale, int B, int H, int S, int D, void* stream) {
+  if (!v_mean) return fail(VDIT_ERR_INVALID_ARG, "%s", "null pointer: v_mean");
+  return quant_fp8(q, k, v, q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks, v_mean, nullptr,
+                   v_scale, nullptr, 0, B, H, S, D, stream, true);
+}
+
+size_t vdit_attn_quant_fp8_noalloc_max_workspace(void) { return vdit::noalloc_scratch_bytes(); }
 
 vdit_status vdit_attn_quant_fp8_vsmooth(const void* q, const void* k, const void* v, void* q8,
                                         void* k8, void* v8, float* q_scale, float* k_scale,

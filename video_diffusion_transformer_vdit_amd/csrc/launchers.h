@@ -28,6 +28,12 @@ hipError_t launch_quant_fp8(const void* q, const void* k, const void* v,
                             float* v_scale, void* workspace, int B, int H, int S,
                             hipStream_t stream);
 
+// Allocation-free pre-pass: the library's own device scratch (noalloc.hip),
+// its size, and its address on the current device (which the stream, if
+// not null, must belong to).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                const float* q_scale, const float* k_scale,
                                const float* k_mean, int k_mean_blocks,
