@@ -19,7 +19,9 @@
 //    4-7 run one phase apart, so each SIMD overlaps one wave's exponentials
 //    with the other wave's MFMAs; a workgroup barrier ends every phase.
 //    Within a matrix phase every LDS operand read is issued six MFMAs ahead
-//    of its use.
+//    of its use, and the wave runs at a raised issue priority (s_setprio) so
+//    that the other wave's exponentials fill the MFMA wave's gaps rather than
+//    delaying its MFMAs.
 //  * K/V tiles go straight from global memory to LDS (global_load_lds_dwordx4,
 //    no register staging) into three-deep rings.  Each load instruction
 //    covers four whole 256-byte rows, so global reads are fully coalesced.
@@ -379,6 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   // barrier that precedes its first use.
   const bool group_a = wave < 4;
   auto phase1 = [&](int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(0);
     prefetch_list(t);
     update_max();
     softmax_p();
@@ -394,6 +397,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(
   };
   auto phase2 = [&](int t, const char* kn, const char* vc, const void* kfill, const void* vfill)
                     __attribute__((always_inline)) {
+    // the matrix phase's wave takes the SIMD's issue slots first: 1.5%
+    // faster dense, 7% block-sparse (the reverse order: 1.4% slower)
+    __builtin_amdgcn_s_setprio(2);
     // steps past the end reload the last tile into a free buffer
     issue_k(kMode == kSparse ? __builtin_amdgcn_readfirstlane((int)(pre_k & 0x3fffu)) : tile_of(t + 3),
             kfill);
