@@ -17,6 +17,8 @@
  * Conventions shared by every entry point:
  *  - Tensors are caller-owned DEVICE memory, layout [B, H, S, D], contiguous,
  *    D fastest.  D must be 128.  Pointers must be 16-byte aligned.
+ *    1 <= S <= VDIT_MAX_SEQ (2^30) and B*H*ceil(S/128) < 2^31, else
+ *    VDIT_ERR_UNSUPPORTED (block-sparse masks: S <= 2^20).
  *  - The library never allocates, frees or synchronises; work is enqueued on
  *    `stream` (a hipStream_t; NULL = the default stream) and runs
  *    asynchronously.  Buffers must stay valid until the stream reaches it.
@@ -40,6 +42,7 @@ extern "C" {
 #define VDIT_ABI_VERSION 1
 #define VDIT_HEAD_DIM 128
 #define VDIT_FP8_BLOCK 64 /* tokens per Q/K fp8 scale block and K mean block */
+#define VDIT_MAX_SEQ (1 << 30) /* largest S any entry point accepts */
 
 typedef enum vdit_status {
   VDIT_OK = 0,

@@ -70,6 +70,8 @@ def fwd(q=A, k=A * 2, v=A * 3, o=A * 4, B=1, H=1, S=16, D=128, scale=0.1, dtype=
     (dict(dtype=1), 2, "dtype"),
     (dict(o=A, q=A), 1, "overlaps"),
     (dict(B=1 << 16, H=1 << 16, S=1 << 10), 2, "too large"),
+    (dict(S=(1 << 30) + 1), 2, "2^30"),
+    (dict(S=(1 << 31) - 1), 2, "2^30"),
 ])
 def test_fwd_validation(kw, status, msg):
     st, err = fwd(**kw)
@@ -208,3 +210,13 @@ def test_fp8_masks_reject_block_v_means():
          "v_bmean": torch.empty((1, 1, 128, 16), dtype=torch.bfloat16)}
     with pytest.raises(ValueError, match="per-channel V mean"):
         binding.vdit_attn_fwd_fp8(z, chunk=32)
+
+
+def test_sizes_refuse_sequences_past_the_limit():
+    """No size query overflows 32-bit token arithmetic: S past 2^30 gives 0."""
+    lib = binding.load()
+    big = (1 << 31) - 1
+    assert lib.vdit_attn_vsmooth_blocks(big) == 0
+    assert lib.vdit_attn_vsmooth_blocks(1 << 30) == -(-(1 << 30) // 128)
+    assert lib.vdit_attn_quant_fp8_workspace_size(1, 1, big, 128, 1) == 0
+    assert lib.vdit_vsmooth_group_workspace_size(1, 1, big, 128, 16) == 0

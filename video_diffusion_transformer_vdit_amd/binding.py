@@ -12,7 +12,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libvdit_attn.so")
+# VDIT_ATTN_LIB points the binding at another build of the same library
+# (e.g. the host-instrumented one the sanitizer test builds)
+LIB_PATH = os.environ.get("VDIT_ATTN_LIB") or os.path.join(PKG, "libvdit_attn.so")
 HEAD_DIM = 128
 FP8_BLOCK = 64
 DTYPE_BF16 = 0

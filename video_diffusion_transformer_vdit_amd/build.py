@@ -84,6 +84,59 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     return LIB_PATH
 
 
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer (each
+# -fsanitize applies to the host pass only; the gfx950 code is built as
+# usual).  For the C-ABI checks on a machine without a GPU.
+SANITIZE_FLAGS = [
+    "-O1", "-g",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (to preload)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("clang") or "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("no shared AddressSanitizer runtime found")
+    return path
+
+
+def build_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """Build the library with sanitized host code into out_dir; returns its
+    path.  Load it with asan_runtime() preloaded (LD_PRELOAD)."""
+    hipcc = _hipcc()
+    os.makedirs(out_dir, exist_ok=True)
+    base = [f for f in HIP_FLAGS if f != "-O3"]
+
+    def compile_one(src):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc, *base, *SANITIZE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, sources()))
+    lib = os.path.join(out_dir, "libvdit_attn_sanitized.so")
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", *objs, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    return lib
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv, save_temps="--save-temps" in sys.argv)
     print(path)

@@ -29,9 +29,12 @@ bool overlaps(const void* a, const void* b, size_t bytes_a, size_t bytes_b) {
 vdit_status check_shape(int B, int H, int S, int D) {
   if (B < 1 || H < 1 || S < 1) return fail(VDIT_ERR_INVALID_ARG, "%s", "B, H and S must be >= 1");
   if (D != VDIT_HEAD_DIM) return fail(VDIT_ERR_UNSUPPORTED, "%s", "only D = 128 is supported");
+  // token indices and limits (up to twice S for block-causal chunks) are
+  // 32-bit in the kernels and in the size arithmetic below
+  if (S > VDIT_MAX_SEQ) return fail(VDIT_ERR_UNSUPPORTED, "%s", "S must be <= 2^30");
   // grid = B*H*ceil(S/128) workgroups must fit a 32-bit grid dimension, and
   // per-head offsets are 64-bit.
-  const long long tiles = (long long)B * H * ((S + 127) / 128);
+  const long long tiles = (long long)B * H * (((long long)S + 127) / 128);
   if (tiles > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL)
     return fail(VDIT_ERR_UNSUPPORTED, "%s", "problem too large for one launch");
   return VDIT_OK;
@@ -194,7 +197,7 @@ vdit_status vdit_attn_quant_fp8_vsmooth(const void* q, const void* k, const void
 }
 
 int vdit_attn_vsmooth_blocks(int S) {
-  if (S < 1) return 0;
+  if (S < 1 || S > VDIT_MAX_SEQ) return 0;
   return vdit::vsmooth_blocks_padded(S);
 }
 
