@@ -407,6 +407,19 @@ def main():
             result["fp8"][key + "_counters"] = {"mfma_busy": c.get("mfma_busy"),
                                                 "valu_active": c.get("valu_active"),
                                                 "clock_ghz": c.get("clock_GHz")} if c else None
+        # the pre-pass writes V codes in the kernel's tiled layout; a boundary
+        # taking token-major [B,H,S,D] codes would add this pass per call
+        v8_tokens = binding.vdit_attn_v8_from_tiles(z["v8"], w.S)
+        v8_tiles = torch.empty_like(z["v8"])
+        ms_r = time_launches(lambda: binding.vdit_attn_v8_to_tiles(v8_tokens, out=v8_tiles),
+                             args.steps, args.warmup)
+        relayout_bytes = w.B * w.H * w.S * w.D + v8_tiles.numel()
+        result["fp8"].update({
+            "v8_to_tiles_ms": round(ms_r, 4),
+            "v8_to_tiles_gbs": round(relayout_bytes / (ms_r * 1e-3) / 1e9, 1),
+            "v8_to_tiles_share_of_attention": round(ms_r / ms_a, 4),
+        })
+        del v8_tokens, v8_tiles
         log("[bench] fp8 block-causal and block-sparse attention (same chunk and map as bf16)")
         for name, kw, flop in (("block_causal", {"chunk": chunk}, causal_flop),
                                ("block_sparse", {"block_mask": mask_dev}, sparse_flop)):

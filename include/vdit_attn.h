@@ -132,6 +132,20 @@ vdit_status vdit_attn_quant_fp8(const void* q, const void* k, const void* v,
                                 void* workspace, size_t workspace_bytes,
                                 int B, int H, int S, int D, void* stream);
 
+/*
+ * E4M3 V codes between the token-major layout [B,H,S,D] (uint8, the layout
+ * of q8 and k8) and the tiled layout above (v8: [B,H,ceil(S/64),D,64]) that
+ * vdit_attn_quant_fp8 writes and every fp8 attention entry point reads.
+ *   to_tiles = 1: src [B,H,S,D] -> dst tiled (keys past S get code 0);
+ *   to_tiles = 0: src tiled -> dst [B,H,S,D].
+ * Both are caller-owned device buffers, 16-byte aligned, not overlapping.
+ * The tiled layout is the fp8 MFMA's P^T key order with a bank swizzle;
+ * keeping it at the boundary saves the attention call this pass (one read
+ * and one write of the codes, bound by HBM bandwidth).  Errors as above.
+ */
+vdit_status vdit_attn_v8_relayout(const void* src, void* dst, int B, int H, int S, int D,
+                                  int to_tiles, void* stream);
+
 /* Bytes of workspace vdit_attn_quant_fp8 needs (0 for invalid shapes). */
 size_t vdit_attn_quant_fp8_workspace_size(int B, int H, int S, int D, int k_mean_blocks);
 

@@ -220,3 +220,17 @@ def test_sizes_refuse_sequences_past_the_limit():
     assert lib.vdit_attn_vsmooth_blocks(1 << 30) == -(-(1 << 30) // 128)
     assert lib.vdit_attn_quant_fp8_workspace_size(1, 1, big, 128, 1) == 0
     assert lib.vdit_vsmooth_group_workspace_size(1, 1, big, 128, 16) == 0
+
+
+def test_v8_relayout_validation():
+    lib = binding.load()
+    st = lib.vdit_attn_v8_relayout(A, A * 4, 1, 2, 200, 128, 2, None)
+    assert st == 1 and b"to_tiles" in lib.vdit_last_error()
+    st = lib.vdit_attn_v8_relayout(None, A * 4, 1, 2, 200, 128, 1, None)
+    assert st == 1 and b"null pointer: src" in lib.vdit_last_error()
+    st = lib.vdit_attn_v8_relayout(A, A + 8, 1, 2, 200, 128, 1, None)
+    assert st == 1 and b"aligned: dst" in lib.vdit_last_error()
+    st = lib.vdit_attn_v8_relayout(A, A + 16 * 1024, 1, 2, 200, 128, 0, None)
+    assert st == 1 and b"overlap" in lib.vdit_last_error()
+    st = lib.vdit_attn_v8_relayout(A, A * 1000, 1, 2, 200, 64, 0, None)
+    assert st == 2 and b"D = 128" in lib.vdit_last_error()

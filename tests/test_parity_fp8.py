@@ -43,12 +43,17 @@ def gpu_quant(q, k, v, k_mean_blocks=None):
 
 def compare_quant(zg, zo, heads=None, what=""):
     """Bit-exact comparison; the GPU's V codes are read back from the
-    kernel's tiled layout first."""
+    kernel's tiled layout first, by the layout's definition (untile_v8) and
+    by the library's own conversion (which must agree)."""
+    import torch
     S = zo["q8"].shape[2]
     for key in KEYS:
         g = zg[key].cpu().numpy()
         if key == "v8":
             g = untile_v8(g, S)
+            lib_tokens = binding.vdit_attn_v8_from_tiles(zg["v8"], S)
+            torch.cuda.synchronize()
+            assert np.array_equal(lib_tokens.cpu().numpy(), g), f"{what}: v8 from tiles"
         o = zo[key]
         if heads is not None:
             g = g[:, heads]
@@ -324,6 +329,21 @@ def test_fp8_joint_key_block_permutation_720p():
     for ec in (False, True):
         model = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows, p_cast="expcast" if ec else "exp")
         check_model(got[("dense", ec)][0], model, f"reversed key blocks, head {h}, expcast={ec}")
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 1000])
+def test_v8_relayout_bit_exact(S):
+    """The library's V-code conversions against the layout's definition
+    (tile_v8 / untile_v8): a byte permutation, exact both ways, keys past S
+    tiled as code 0."""
+    import torch
+    g = np.random.default_rng(S)
+    codes = g.integers(0, 256, (2, 3, S, 128), dtype=np.uint8)
+    tiles = binding.vdit_attn_v8_to_tiles(to_dev_any(codes))
+    back = binding.vdit_attn_v8_from_tiles(tiles, S)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(tiles.cpu().numpy(), tile_v8(codes))
+    np.testing.assert_array_equal(back.cpu().numpy(), codes)
 
 
 def test_fp8_max_sequence_length_sampled():

@@ -45,6 +45,7 @@ SIGNATURES = {
                                        _I, _P]),
     "vdit_attn_fwd_fp8_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F,
                                       _I, _P, _I, _P]),
+    "vdit_attn_v8_relayout": (_I, [_P, _P, _I, _I, _I, _I, _I, _P]),
     "vdit_vsmooth_group_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "vdit_vsmooth_group": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]),
     "vdit_permute_tokens": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
@@ -279,6 +280,39 @@ def vdit_attn_quant_fp8_noalloc(q, k, v, out, stream=None):
         int(z["k_mean"].shape[2]), _dev(z["v_mean"], torch.float32, "v_mean"),
         _dev(z["v_scale"], torch.float32, "v_scale"), B, H, S, D, _stream(stream)))
     return z
+
+
+def vdit_attn_v8_to_tiles(v8_tokens, out=None, stream=None):
+    """uint8 E4M3 V codes [B, H, S, 128] -> the fp8 kernels' tiled layout
+    [B, H, ceil(S/64), 128, 64] (vdit_attn_v8_relayout)."""
+    import torch
+    B, H, S, D = _shape4(v8_tokens)
+    if out is None:
+        with _alloc_on(stream):
+            out = torch.empty((B, H, -(-S // FP8_BLOCK), D, FP8_BLOCK), dtype=torch.uint8,
+                              device=v8_tokens.device)
+    lib = load()
+    check(lib.vdit_attn_v8_relayout(_dev(v8_tokens, torch.uint8, "src"), _dev(out, torch.uint8, "dst"),
+                                    B, H, S, D, 1, _stream(stream)))
+    return out
+
+
+def vdit_attn_v8_from_tiles(v8_tiles, S, out=None, stream=None):
+    """The fp8 kernels' tiled V codes [B, H, ceil(S/64), 128, 64] ->
+    token-major [B, H, S, 128] (vdit_attn_v8_relayout)."""
+    import torch
+    if v8_tiles.dim() != 5:
+        raise ValueError("expected tiled codes [B, H, ceil(S/64), 128, 64]")
+    B, H, nb, D, blk = (int(x) for x in v8_tiles.shape)
+    if blk != FP8_BLOCK or nb != -(-int(S) // FP8_BLOCK):
+        raise ValueError("tile count does not match S")
+    if out is None:
+        with _alloc_on(stream):
+            out = torch.empty((B, H, int(S), D), dtype=torch.uint8, device=v8_tiles.device)
+    lib = load()
+    check(lib.vdit_attn_v8_relayout(_dev(v8_tiles, torch.uint8, "src"), _dev(out, torch.uint8, "dst"),
+                                    B, H, int(S), D, 0, _stream(stream)))
+    return out
 
 
 def vdit_attn_fwd_fp8(z, scale=None, o=None, stream=None, expcast=False, chunk=0, block_mask=None):

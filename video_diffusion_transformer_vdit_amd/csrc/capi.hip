@@ -196,6 +196,20 @@ vdit_status vdit_attn_quant_fp8_vsmooth(const void* q, const void* k, const void
                    v_scale, workspace, workspace_bytes, B, H, S, D, stream);
 }
 
+vdit_status vdit_attn_v8_relayout(const void* src, void* dst, int B, int H, int S, int D,
+                                  int to_tiles, void* stream) {
+  VDIT_TRY(check_ptr(src, "src"));
+  VDIT_TRY(check_ptr(dst, "dst"));
+  VDIT_TRY(check_shape(B, H, S, D));
+  if (to_tiles != 0 && to_tiles != 1) return fail(VDIT_ERR_INVALID_ARG, "%s", "to_tiles must be 0 or 1");
+  const size_t tokens = (size_t)B * H * S * D;
+  const size_t tiles = (size_t)B * H * ((S + VDIT_FP8_BLOCK - 1) / VDIT_FP8_BLOCK) * VDIT_FP8_BLOCK * D;
+  if (overlaps(src, dst, to_tiles ? tokens : tiles, to_tiles ? tiles : tokens))
+    return fail(VDIT_ERR_INVALID_ARG, "%s", "src and dst overlap");
+  return hip_result(vdit::launch_v8_layout(src, dst, B, H, S, to_tiles == 1,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int vdit_attn_vsmooth_blocks(int S) {
   if (S < 1 || S > VDIT_MAX_SEQ) return 0;
   return vdit::vsmooth_blocks_padded(S);

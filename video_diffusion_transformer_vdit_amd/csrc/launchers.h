@@ -42,6 +42,10 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                                bool expcast, int chunk, const void* block_mask,
                                hipStream_t stream);
 
+// E4M3 V codes between token-major [B,H,S,128] and the fp8 kernel's tiles
+hipError_t launch_v8_layout(const void* src, void* dst, int B, int H, int S, bool to_tiles,
+                            hipStream_t stream);
+
 // V-Smooth Group: k-means of V tokens and the stable cluster permutation
 constexpr int kGroupMaxClusters = 4096;
 size_t group_workspace_bytes(int B, int H, int S, int k);
