@@ -347,22 +347,28 @@ def test_v8_relayout_bit_exact(S):
 
 
 def test_fp8_max_sequence_length_sampled():
-    """S = 2^20 (one head) through the GPU pre-pass and fp8 attention; sampled
-    rows against the quantisation model on the oracle's own pre-pass."""
+    """S = 2^20 (one head) through the GPU pre-pass and fp8 attention with
+    both weight casts; sampled rows against the quantisation model on the
+    oracle's own pre-pass."""
     import torch
     S = 1 << 20
     q, k, v = rand_bits((1, 1, S, 128), 91), rand_bits((1, 1, S, 128), 92, 1.0, 0.5), \
         rand_bits((1, 1, S, 128), 93, 1.0, 1.0)
     log(f"fp8 max length S={S}")
     z = gpu_quant(q, k, v)
-    o = binding.vdit_attn_fwd_fp8(z, scale=SCALE)
-    torch.cuda.synchronize()
     rows = np.array([0, 1, 4097, S // 2, S - 1])
-    got = o[0, 0, rows].float().cpu().numpy().astype(np.float64)
-    del o, z
+    got = {}
+    for ec in (False, True):
+        o = binding.vdit_attn_fwd_fp8(z, scale=SCALE, expcast=ec)
+        torch.cuda.synchronize()
+        got[ec] = o[0, 0, rows].float().cpu().numpy().astype(np.float64)
+        del o
+    del z
     torch.cuda.empty_cache()
     zh = ofp8.quantize_head(q[0, 0], k[0, 0], v[0, 0])
-    check_model(got, ofp8.attention_fp8_model_head(zh, SCALE, rows=rows), f"fp8 S={S}")
+    for ec in (False, True):
+        ref = ofp8.attention_fp8_model_head(zh, SCALE, rows=rows, p_cast="expcast" if ec else "exp")
+        check_model(got[ec], ref, f"fp8 S={S} expcast={ec}")
 
 
 # ---- key masks (block-causal chunks, block-sparse tile maps) on the fp8 path ----
