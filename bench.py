@@ -172,12 +172,17 @@ def calibration_copy(n_bytes=1 << 31, reps=3):
     print(json.dumps({"calibration_copy_bytes": n_bytes, "reps": reps}), flush=True)
 
 
-def cpu_baseline(w, q, k, v, scale, seconds):
+def cpu_baseline(w, q, k, v, scale, seconds, gpu_head0=None):
     """fp64 oracle (as it stands) on head 0, 256-row chunks until `seconds`
     have elapsed; rate scaled to TFLOP/s of the same attention arithmetic.
     The oracle's matrix products run on numpy's BLAS threads, so `cores` is
     that thread count; the host's logical CPUs and the process's affinity
-    set are reported beside it."""
+    set are reported beside it.  With `gpu_head0` (the timed kernel's bf16
+    output bits of head 0, [S, D]) the rows the oracle computed also check
+    that output: max-abs and L1 mean-rel against the oracle rounded to bf16,
+    and how many elements exceed 1e-2 and by how many bf16 steps of their
+    magnitude at most (outside the timed loop, which the comparison does not
+    slow)."""
     from oracle import attention as oa
     affinity = len(os.sched_getaffinity(0))
     try:
@@ -189,14 +194,37 @@ def cpu_baseline(w, q, k, v, scale, seconds):
     t0 = time.perf_counter()
     chunk = 256
     start = 0
+    outs = []
     while True:
         rows = np.arange(start, min(w.S, start + chunk))
-        oa.attention_head(q[0, 0], k[0, 0], v[0, 0], scale, rows=rows)
+        ref = oa.attention_head(q[0, 0], k[0, 0], v[0, 0], scale, rows=rows)
+        if gpu_head0 is not None and len(outs) * chunk < w.S:
+            outs.append((rows, ref))
         rows_done += rows.size
         start = (start + chunk) % w.S
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    check = {}
+    if gpu_head0 is not None and outs:
+        num = den = 0.0
+        worst = worst_steps = 0.0
+        n = n_over = 0
+        for rows, ref in outs:
+            ref_b = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+            got = inputs.bf16_bits_to_f32(gpu_head0[rows]).astype(np.float64)
+            err = np.abs(got - ref_b)
+            num += float(err.sum())
+            den += float(np.abs(ref_b).sum())
+            worst = max(worst, float(err.max()))
+            over = err > 1e-2
+            n_over += int(over.sum())
+            if over.any():
+                # one bf16 step of the reference: 2^-7 relative
+                worst_steps = max(worst_steps, float((err[over] / (2.0 ** -7 * np.abs(ref_b[over]))).max()))
+            n += rows.size
+        check = {"check_rows": n, "max_abs_vs_oracle": worst, "mean_rel_vs_oracle": num / den,
+                 "elements_over_1e-2": n_over, "over_1e-2_max_bf16_steps": worst_steps}
     flop = rows_done * 4.0 * w.S * w.D
     return {
         "value": flop / dt / 1e12,
@@ -208,6 +236,7 @@ def cpu_baseline(w, q, k, v, scale, seconds):
         "kind": "oracle",
         "sample": (f"{rows_done} query rows of head 0 of {w.name} (S={w.S}), fp64 numpy, "
                    f"{dt:.1f} s; full call extrapolates to {w.flop / (flop / dt):.0f} s"),
+        **check,
     }
 
 
@@ -294,6 +323,8 @@ def main():
     log("[bench] bf16 attention")
     ms, per_launch, clocks = time_launches(lambda: binding.vdit_attn_fwd(q, k, v, o=o, scale=scale),
                                            args.steps, args.warmup, detail=True)
+    # head 0 of the timed kernel's output, for the CPU leg's check
+    head0 = o[0, 0].view(torch.int16).cpu().numpy().view(np.uint16)
     tflops = w.flop / (ms * 1e-3) / 1e12
     sclk = float(np.median(clocks)) if clocks else None
     headline = w.name == HEADLINE
@@ -464,7 +495,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, scale, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, scale, args.cpu_seconds, head0)
     print(json.dumps(result), flush=True)
 
 

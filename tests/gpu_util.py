@@ -9,9 +9,12 @@ import numpy as np
 from video_diffusion_transformer_vdit_amd import inputs
 
 # bf16 bars (against the oracle rounded to bf16, the closest an output in
-# bf16 can get): max-abs <= 1e-2, L1 mean-rel <= 2e-3.
+# bf16 can get): max-abs <= 1e-2, L1 mean-rel <= 2e-3.  Where |O| >= 2 one
+# bf16 step (2^-7 relative) is wider than 1e-2 and an element may instead be
+# one step away; the share of elements that use this is held to 1e-4.
 BF16_MAX_ABS = 1e-2
 BF16_MEAN_REL = 2e-3
+BF16_OVER_SHARE = 1e-4
 # fp8 bars of the method's statement: cosine >= 0.999, max-abs <= 5e-2.
 FP8_COS = 0.999
 FP8_MAX_ABS = 5e-2
