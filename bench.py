@@ -47,8 +47,9 @@ def time_launches(fn, steps, warmup, detail=False):
     HIP events recorded on torch's current stream (the launch stream).
 
     With `detail`, an event also follows every launch, and while the launches
-    run the host samples the graphics clock from sysfs; it then returns
-    (average ms, per-launch ms list, clock samples in MHz)."""
+    run the host samples the graphics clock and the socket power from sysfs;
+    it then returns (average ms, per-launch ms list, clock samples in MHz,
+    power samples in W)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -60,18 +61,22 @@ def time_launches(fn, steps, warmup, detail=False):
         if detail:
             marks[i + 1].record()
     marks[-1].record()
-    clocks = []
+    clocks, powers = [], []
     path = sclk_path() if detail else None
-    while path and not marks[-1].query():
-        mhz = read_sclk(path)
+    ppath = power_path() if detail else None
+    while (path or ppath) and not marks[-1].query():
+        mhz = read_sclk(path) if path else None
         if mhz is not None:
             clocks.append(mhz)
+        watts = read_power(ppath) if ppath else None
+        if watts is not None:
+            powers.append(watts)
         time.sleep(0.01)
     torch.cuda.synchronize()
     avg = marks[0].elapsed_time(marks[-1]) / steps
     if not detail:
         return avg
-    return avg, [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)], clocks
+    return avg, [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)], clocks, powers
 
 
 def sclk_path():
@@ -86,6 +91,36 @@ def sclk_path():
         return path
     found = [f for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk") if os.access(f, os.R_OK)]
     return found[0] if len(found) == 1 else None
+
+
+def power_path():
+    """The hwmon file with the socket power of torch's device 0 (microwatts),
+    or None if the driver exposes none readable."""
+    import glob
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+    for name in ("power1_average", "power1_input"):
+        found = [f for f in glob.glob(os.path.join(dev, "hwmon", "hwmon*", name)) if os.access(f, os.R_OK)]
+        if found and read_power(found[0]) is not None:
+            return found[0]
+    return None
+
+
+def power_cap():
+    """The socket power cap in W (hwmon power1_cap beside the power file), or None."""
+    path = power_path()
+    return read_power(os.path.join(os.path.dirname(path), "power1_cap")) if path else None
+
+
+def read_power(path):
+    """Socket power in W from a hwmon file in microwatts, or None."""
+    try:
+        with open(path) as f:
+            uw = int(f.read().strip())
+    except (OSError, ValueError):
+        return None
+    return uw / 1e6 if uw > 0 else None
 
 
 def read_sclk(path):
@@ -321,7 +356,7 @@ def main():
     q, k, v = dev(qb), dev(kb), dev(vb)
     o = torch.empty_like(q)
     log("[bench] bf16 attention")
-    ms, per_launch, clocks = time_launches(lambda: binding.vdit_attn_fwd(q, k, v, o=o, scale=scale),
+    ms, per_launch, clocks, powers = time_launches(lambda: binding.vdit_attn_fwd(q, k, v, o=o, scale=scale),
                                            args.steps, args.warmup, detail=True)
     # head 0 of the timed kernel's output, for the CPU leg's check
     head0 = o[0, 0].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -372,6 +407,11 @@ def main():
         # the dense bf16 peak rescaled from the 2.4 GHz nameplate to it
         "sclk_mhz": {"median": sclk, "min": min(clocks) if clocks else None,
                      "max": max(clocks) if clocks else None, "samples": len(clocks)},
+        # socket power sampled the same way: the kernel runs at the power cap,
+        # which sets the clock above
+        "socket_power_w": {"median": round(float(np.median(powers)), 1) if powers else None,
+                           "max": round(max(powers), 1) if powers else None, "samples": len(powers),
+                           "cap": power_cap()},
         "peak_at_observed_clock": round(PEAK_BF16_TFLOPS * sclk / 2400.0, 1) if sclk else None,
         "frac_at_observed_clock": round(tflops / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4) if sclk else None,
     }
