@@ -81,6 +81,33 @@ def test_scales():
         check_close(got, oa.attention(*x, scale), f"scale={scale}", ulp_slack=True)
 
 
+def test_tiny_scale_gives_the_mean_of_v():
+    """scale -> 0 makes every weight equal: the output is the mean of V
+    (within the output's bf16 rounding)."""
+    g = np.random.default_rng(12)
+    x = [inputs.f32_to_bf16_bits(g.standard_normal((1, 2, 500, 128)).astype(np.float32)) for _ in range(3)]
+    scale = 1e-8
+    got = f32_of(run(*x, scale=scale))
+    check_close(got, oa.attention(*x, scale), "scale=1e-8")
+    mean_v = inputs.bf16_bits_to_f32(x[2]).astype(np.float64).mean(axis=2, keepdims=True)
+    err = np.abs(got - mean_v)
+    log(f"scale=1e-8 vs mean of V: max_abs={err.max():.3e}")
+    assert np.all(err <= np.maximum(4e-3, 2.0 ** -7 * np.abs(mean_v)))
+
+
+def test_query_permutation_permutes_rows_bitwise():
+    """Every query row is computed on its own (its lane's softmax state,
+    exact power-of-two rescales), so permuting the rows of Q permutes the
+    rows of O bit for bit, ragged last tile included."""
+    g = np.random.default_rng(11)
+    q, k, v = (inputs.f32_to_bf16_bits(g.standard_normal((1, 2, 777, 128)).astype(np.float32))
+               for _ in range(3))
+    perm = g.permutation(777)
+    a = bits_of(run(q, k, v))
+    b = bits_of(run(np.ascontiguousarray(q[:, :, perm]), k, v))
+    assert np.array_equal(a[:, :, perm], b)
+
+
 def test_large_scale_returns_the_argmax_row():
     """Large scale with a unique maximum gives the value row of the best key
     (the softmax's limit).  At scale 50 a row whose best score leads the
