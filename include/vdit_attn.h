@@ -187,7 +187,8 @@ size_t vdit_attn_quant_fp8_noalloc_max_workspace(void);
  * that of the quantised weights, so the weights of a row sum to one and the
  * mean restore is exact (VC-Attention article, section 02, Restore):
  *   o = v_scale * (sum_j P8_ij v8_j) / (sum_j P8_ij) + v_mean, bf16 out.
- * Float arrays must be 16-byte aligned.
+ * Float arrays must be 16-byte aligned; o may not overlap q8, k8 or v8
+ * (VDIT_ERR_INVALID_ARG).
  */
 vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                               const float* q_scale, const float* k_scale,
@@ -201,11 +202,16 @@ vdit_status vdit_attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * same arguments and result definition, except that the P8 byte is written
  * directly from the log domain instead of exp2 followed by an E4M3
  * conversion.  The E4M3 byte of v read as an integer is about 8 log2(v) + 56;
- * with the article's centring constant -0.35 and P scaled by 448:
- *   P8_ij = rne(8 (t_ij - m_i) + 8 log2(448) + 55.65), clamped to [0, 255]
- * (t <= m keeps it <= 126, the code of 448; bytes below 8 decode as E4M3
- * subnormals).  One FMA and one convert per weight; it agrees with the exact
- * byte in about 79.6% of weights and is otherwise one code away.
+ * with the article's centring constant -0.35 and P scaled by 448, the byte
+ * position of a weight is z_ij = 8 (t_ij - m_i) + 8 log2(448) + 55.65
+ * (t <= m keeps it <= 126, the code of 448).  Where z >= 7.5 the code is
+ * rne(z), the article's byte; below, where codes 1-7 are E4M3 subnormals
+ * rather than points of the log map, it is the subnormal nearest the value
+ * 2^(floor(z/8) - 7) (1 + (z mod 8)/8) that the same map gives to z, so a
+ * weight is always within one code of the exact cast and scales by exact
+ * powers of two with the reference.  One FMA and two converts per weight;
+ * it agrees with the exact byte in about 79.6% of weights in the normal
+ * range.
  */
 vdit_status vdit_attn_fwd_fp8_expcast(const void* q8, const void* k8, const void* v8,
                                       const float* q_scale, const float* k_scale,

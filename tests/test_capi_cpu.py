@@ -182,6 +182,17 @@ def test_vsmooth_group_validation():
     assert st == 1 and b"overlaps" in lib.vdit_last_error()
 
 
+def test_fp8_output_must_not_overlap_the_codes():
+    lib = binding.load()
+    far = 1 << 40
+    S, nb = 200, 4
+    ptrs = [A + i * far for i in range(10)]  # q8 k8 v8 q_scale k_scale k_mean v_mean v_scale o
+    q8, k8, v8, qs, ks, km, vm, vs, o = ptrs[:9]
+    for alias in (q8, k8, v8, v8 + 256 * 128):
+        st = lib.vdit_attn_fwd_fp8(q8, k8, v8, qs, ks, km, nb, vm, vs, alias, 1, 2, S, 128, 0.1, None)
+        assert st == 1 and b"o overlaps" in lib.vdit_last_error()
+
+
 def test_fp8_masked_validation():
     lib = binding.load()
     args = (A, A, A, A, A, A, 4, A, A, A, 1, 2, 200, 128, 0.1)

@@ -246,6 +246,12 @@ static vdit_status fwd_fp8(const void* q8, const void* k8, const void* v8, const
     return fail(VDIT_ERR_UNSUPPORTED, "%s", "k_mean_blocks must be 1 or ceil(S/64)");
   if (block_mask && (S + 63) / 64 > 16384)
     return fail(VDIT_ERR_UNSUPPORTED, "%s", "block-sparse attention supports S <= 1048576");
+  // the bf16 output must not overlap the codes it is computed from
+  const size_t codes = (size_t)B * H * S * D;
+  const size_t tiles = (size_t)B * H * nb * VDIT_FP8_BLOCK * D;
+  if (overlaps(o, q8, 2 * codes, codes) || overlaps(o, k8, 2 * codes, codes) ||
+      overlaps(o, v8, 2 * codes, tiles))
+    return fail(VDIT_ERR_INVALID_ARG, "%s", "o overlaps an input");
   return hip_result(vdit::launch_attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, k_mean, k_mean_blocks,
                                               v_mean, v_bmean, v_scale, o, B, H, S, scale, expcast,
                                               chunk, block_mask, static_cast<hipStream_t>(stream)));
