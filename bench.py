@@ -407,8 +407,8 @@ def main():
         # the dense bf16 peak rescaled from the 2.4 GHz nameplate to it
         "sclk_mhz": {"median": sclk, "min": min(clocks) if clocks else None,
                      "max": max(clocks) if clocks else None, "samples": len(clocks)},
-        # socket power sampled the same way: the kernel runs near the power cap,
-        # (the cap beside it), where the power management holds the clock above
+        # socket power sampled the same way, with the cap beside it: the kernel
+        # runs near the cap, where the power management holds the clock above
         "socket_power_w": {"median": round(float(np.median(powers)), 1) if powers else None,
                            "max": round(max(powers), 1) if powers else None, "samples": len(powers),
                            "cap": power_cap()},
