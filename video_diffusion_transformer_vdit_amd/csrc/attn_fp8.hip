@@ -22,14 +22,14 @@
 // quantised as P8 = E4M3(448 p) for the fp8 PV product; because m only moves
 // by whole powers of two, the quantised weights equal those taken against
 // the final row maximum (outside the subnormal range).  The row sum is that
-// of the quantised weights, formed by one more fp8 MFMA per tile against an
-// all-ones operand, so the weights of a row sum to exactly one and the mean
-// restore is exact.  Epilogue: o = v_scale (sum_j P8_ij v8_j) / (sum_j P8_ij)
-// + v_mean.
+// of the quantised weights, formed by one 16x16x128 fp8 MFMA per tile (half
+// the cycles of a 32x32x64 one) against a 0/1 selection operand, so the
+// weights of a row sum to exactly one and the mean restore is exact.
+// Epilogue: o = v_scale (sum_j P8_ij v8_j) / (sum_j P8_ij) + v_mean.
 //
 // With V block means (the article's Demean over 128-token hardware blocks)
-// the restore runs inside the key loop instead: the row-sum MFMA uses a
-// one-hot operand whose single row of ones is the block's slot, so it
+// the restore runs inside the key loop instead: the row sum is a 32x32x64
+// MFMA against a one-hot operand whose single row of ones is the block's slot, so it
 // accumulates each block's weight sum in its own row (16 blocks = 32 tiles
 // per batch); after each batch two bf16 MFMAs per 32 channels (the exact
 // bf16 means against the high and low bf16 parts of the sums, about 2^-16
@@ -86,6 +86,10 @@ __device__ __forceinline__ uint32_t cvt_u32_sat(float x) {
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // operand formats 0/0 = E4M3 x E4M3; no block scales
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p, bool ok) {
@@ -437,15 +441,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
-  // row sum of the quantised weights: every row of ones x P^T is the column sum
+  // with V block means: per-block weight sums (see pv below)
   f32x16 lacc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
-  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
-  // opaque from here on: kept in its eight registers rather than copied back
-  // from one register before every row-sum MFMA
-  if (!kVBlock) asm volatile("" : "+v"(ones));
+  // Row sum of the quantised weights on a 16x16x128 MFMA whose B operand is
+  // the P registers of the 32x32x64 PV product as they stand: lane l then
+  // stands for column l % 16 and k-group l / 16, i.e. query l % 16 + 16 (g % 2)
+  // with keys 32 (g / 2) .. + 31 of the tile (g = l / 16).  Rows 0 and 8 of
+  // the selection operand take k-groups 0 and 2 (queries 0-15), rows 4 and 12
+  // groups 1 and 3 (queries 16-31), so element 0 of lane l's output (row
+  // 4 (l / 16), column l % 16) is the weight sum of the lane's own query.
+  f32x4 rsum = {0.f, 0.f, 0.f, 0.f};
+  const int sel_row = lane & 15, sel_grp = lane >> 4;
+  const bool sel_on =
+      (sel_grp & 1) ? (sel_row == 4 || sel_row == 12) : (sel_row == 0 || sel_row == 8);
+  const int sel_b = sel_on ? 0x38383838 : 0;  // E4M3 1.0 or 0
+  i32x8 sel = {sel_b, sel_b, sel_b, sel_b, sel_b, sel_b, sel_b, sel_b};
+  // opaque from here on: kept in its eight registers rather than rebuilt
+  // before every row-sum MFMA
+  if (!kVBlock) asm volatile("" : "+v"(sel));
   // finite when block-sparse: tiles scored entirely -inf before a row's first
   // allowed key then give weight 0, not NaN
   float m_ref = kMode == kSparse ? -1e30f : -INFINITY;
@@ -515,8 +530,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       const float mq = max_halves(mnew);
       const float mnext = mq > m_ref ? ceilf(mq) : m_ref;
       const float alpha = exp2_fast(m_ref - mnext);
-      lacc *= alpha;
-      if (kVBlock) l_tot *= alpha;
+      if (kVBlock) {
+        lacc *= alpha;
+        l_tot *= alpha;
+      } else {
+        rsum *= alpha;
+      }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
       m_ref = mnext;
@@ -578,7 +597,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       const i32x8 onehot = {o, o, o, o, o, o, o, o};
       lacc = mfma32x32x64_fp8(onehot, pb, lacc);
     } else {
-      lacc = mfma32x32x64_fp8(ones, pb, lacc);
+      rsum = mfma16x16x128_fp8(sel, pb, rsum);
     }
   };
 
@@ -714,7 +733,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     vload((nkt - 1) >> 5);
     vdrain();
   }
-  const float lsum = kVBlock ? l_tot : lacc[0];
+  const float lsum = kVBlock ? l_tot : rsum[0];
   // a row with no allowed key (block-sparse) has l = 0 and outputs zeros
   const bool empty_row = kMode == kSparse && lsum == 0.f;
   const float inv = empty_row ? 0.f : 1.0f / lsum;
