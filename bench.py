@@ -81,7 +81,7 @@ def time_launches(fn, steps, warmup, detail=False):
 
 def sclk_path():
     """The sysfs file that lists the graphics clock levels of torch's device
-    0, the current one marked with '*'; None if the driver exposes none."""
+    0, the current one marked with '*'; None if sysfs has no readable one."""
     import glob
     import torch
     p = torch.cuda.get_device_properties(0)
@@ -95,7 +95,7 @@ def sclk_path():
 
 def power_path():
     """The hwmon file with the socket power of torch's device 0 (microwatts),
-    or None if the driver exposes none readable."""
+    or None if sysfs has no readable one."""
     import glob
     import torch
     p = torch.cuda.get_device_properties(0)
